@@ -1,0 +1,210 @@
+"""Throughput of the fused attention forward pass on one MI355X.
+
+One step = one fa_forward call over the whole workload: the Llama-3-8B layer
+shape (batch 1, 32 heads, n = 8192, d_k = 128, bf16, causal) by default.
+Inputs are seeded synthetic N(0,1) tensors, resident in HBM before timing.
+FLOPs follow the two-GEMM count 4*b*h*n^2*d_k, halved for a causal mask.
+
+Prints one JSON line with the throughput, the roofline position of the
+kernel (achieved TFLOP/s against the dense MFMA peak of its dtype, plus the
+HBM traffic measured by rocprofv3 counters when the stored measurement
+belongs to the current kernel source) and the CPU oracle timed on a bounded
+sample of the same workload on this host's cores.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --copy-calibration      # plain copy of known size (counter scale)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s & % of bf16 MFMA peak (h32, n8192, d_k128, causal)"
+# Dense MFMA peaks of MI355X, TFLOP/s (256 CUs x FLOP/clk/CU x 2.4 GHz; the
+# published 2.5 PFLOP/s bf16/fp16, 5.0 fp8 and 157.3 fp32 figures).
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "fp8": 5033.2, "f32": 157.3}
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ("transformer_attention_08_amd/csrc/fa_fwd.hip",
+                  "transformer_attention_08_amd/csrc/fa_api.cpp",
+                  "transformer_attention_08_amd/csrc/fa_kernels.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama3_8b_bf16_causal.json")
+
+
+def algorithmic_flops(w) -> float:
+    """The two GEMMs, 2*n*n*d_k FLOP each per head; halved under a causal mask."""
+    f = 4.0 * w.batch * w.heads * w.n * w.n * w.d_k
+    return f / 2 if w.causal else f
+
+
+def min_hbm_bytes(w) -> int:
+    """Read Q, K, V once; write O and the fp32 LSE once."""
+    elt = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+    rows = w.batch * w.heads * w.n
+    return rows * w.d_k * (3 * elt[w.dtype] + elt[w.out_dtype]) + 4 * rows
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload_name: str):
+    """HBM bytes per launch from the committed counter summary, if current."""
+    if workload_name != "llama3_8b_bf16_causal" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, budget_s: float = 15.0):
+    """The fp64 oracle on whole heads of the same inputs, as many heads as fit
+    the time budget (at least one); TFLOP/s under the same FLOP count."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    qb, kb, vb = inp.bits("q"), inp.bits("k"), inp.bits("v")
+    done, elapsed = 0, 0.0
+    while done < w.heads * w.batch:
+        bi, hi = divmod(done, w.heads)
+        q = oracle.decode(qb[bi:bi + 1, hi:hi + 1], w.dtype, inp.q_descale)
+        k = oracle.decode(kb[bi:bi + 1, hi:hi + 1], w.dtype, inp.k_descale)
+        v = oracle.decode(vb[bi:bi + 1, hi:hi + 1], w.dtype, inp.v_descale)
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, w.scale, w.causal)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        if elapsed >= budget_s or elapsed / done * (done + 1) > 2 * budget_s:
+            break
+    fl = 4.0 * done * w.n * w.n * w.d_k / (2 if w.causal else 1)
+    return {"value": fl / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {w.batch * w.heads} heads, all {w.n} rows each, fp64 NumPy, "
+                      f"{elapsed:.1f} s"}
+
+
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
+    """A plain device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
+    import torch
+
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3_8b_bf16_causal")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention forward runs on a single MI355X "
+              "here (heads would shard across GPUs with no communication); run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+
+    import torch
+
+    import transformer_attention_08_amd as fa
+    import workload
+
+    w = workload.WORKLOADS[args.workload]
+    fa.load_library()
+    inp = workload.workload_inputs(w, args.seed)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = inp.to(dev)
+    o = torch.empty(w.batch, w.heads, w.n, w.d_k, dtype=workload.torch_dtype(w.out_dtype), device=dev)
+    lse = torch.empty(w.batch, w.heads, w.n, dtype=torch.float32, device=dev)
+
+    def step():
+        if w.dtype == "fp8":
+            fa.forward_fp8(d.q, d.k, d.v, inp.q_descale, inp.k_descale, inp.v_descale,
+                           causal=w.causal, scale=w.scale, out=o, lse=lse)
+        else:
+            fa.forward(d.q, d.k, d.v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} calls)", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)  # the stream fa_forward enqueues on
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    total_ms = evs[0].elapsed_time(evs[-1])
+    ms = total_ms / args.steps
+
+    flops = algorithmic_flops(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = stored_traffic(w.name)
+    line = {
+        "metric": METRIC if w.name == "llama3_8b_bf16_causal" else f"attn fwd TFLOP/s ({w.name})",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "n": w.n, "d_k": w.d_k,
+                   "causal": w.causal, "flops_per_step": flops},
+        "pct_of_peak": round(100.0 * tflops / peak, 2),
+        "ms_median": round(statistics.median(per), 5),
+        "ms_min": round(min(per), 5),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": traffic,
+                     "kernel": "fwd_mfma16" if w.dtype != "f32" else "fwd_mfma32",
+                     "min_hbm_bytes": min_hbm_bytes(w)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,122 @@
+/*
+ * fa.h -- C ABI of the fused attention forward pass for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * What is computed (slides "Case study: FlashAttention", slide "Attention is
+ * where tokens meet", the attention equation; per-row form on the slide
+ * "Problem: softmax needs the whole row"):
+ *
+ *     S   = scale * Q K^T + mask          (mask: 0 visible, -inf excluded)
+ *     O   = softmax_rows(S) V
+ *     LSE = ln sum_j exp(S_ij)            (per query row, natural log)
+ *
+ * for every (batch, head) independently (slide "Queries, keys and values":
+ * after the head split each head is an [n x d_k] problem of its own). The
+ * causal mask excludes key j from query i when j > i. The kernel never
+ * stores S or P; it merges key/value tiles with the online-softmax
+ * recurrence of the slide "Online softmax: divide once, at the end" and
+ * divides by the row sum once per row. The log-sum-exp row statistic is the
+ * quantity that lets partial results over disjoint key blocks be combined
+ * later ("Mastering FlashAttention: The Algebraic Foundation", deep-insight
+ * takeaways).
+ *
+ * Layout. q, k, v and o are dense row-major [batch, heads, n, d_k] arrays
+ * with d_k fastest (the [h x n x d_k] head split of the slide "Queries, keys
+ * and values" with a leading batch axis). lse is dense fp32 [batch, heads,
+ * n]. All pointers are device pointers on the current HIP device.
+ *
+ * Element types. q, k and v share one type. o has the input type for
+ * FA_F32, FA_F16 and FA_BF16, and is bf16 for FA_FP8_E4M3 (OCP e4m3 "fn",
+ * largest finite 448, no infinities). Accumulation is fp32.
+ *
+ * Supported shapes. batch, heads >= 1; n >= 1 (any n: ragged tails are
+ * masked inside the kernel); d_k in {64, 128}; causal in {0, 1}; scale
+ * finite and >= 0 (the method's scale is 1/sqrt(d_k); the library folds
+ * log2(e) into it and evaluates exponentials as exp2).
+ *
+ * Ownership. The caller owns every buffer. The library allocates no device
+ * or host memory per call, keeps no workspace and no n x n buffer, and holds
+ * no state beyond per-process kernel registration. q, k, v are only read.
+ * o and lse are written in full (every element of the valid rows) and must
+ * not overlap q, k, v or each other. Calls are reentrant and thread-safe.
+ *
+ * Errors. Every entry point returns an fa_status. Arguments are validated on
+ * the host before any HIP call; on a validation error nothing is launched
+ * and no output byte is written. FA_ERR_HIP means the HIP runtime refused
+ * the device query or the launch (for example: no GPU); fa_last_hip_error()
+ * then returns the hipError_t code for the calling thread. The call is
+ * asynchronous: it returns once the kernel is enqueued on `stream` (a
+ * hipStream_t; NULL means the null stream). Faults inside the kernel surface
+ * at the caller's next synchronisation with that stream, and the buffers
+ * must stay alive until the stream has passed the kernel.
+ */
+#ifndef FA_MI355X_FA_H
+#define FA_MI355X_FA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_F32 = 0,       /* IEEE binary32                                  */
+  FA_F16 = 1,       /* IEEE binary16                                  */
+  FA_BF16 = 2,      /* bfloat16 (upper half of a binary32)            */
+  FA_FP8_E4M3 = 3   /* OCP 8-bit E4M3 "fn" (bias 7, max 448, no inf)  */
+} fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* q, k, v or o is NULL                                   */
+  FA_ERR_SHAPE = 2,       /* batch, heads or n < 1                                  */
+  FA_ERR_DTYPE = 3,       /* dtype is not one of fa_dtype                           */
+  FA_ERR_UNSUPPORTED = 4, /* d_k not in {64, 128}, or causal not in {0, 1}          */
+  FA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                       */
+  FA_ERR_SCALE = 6,       /* scale (or a descale) is not finite, or is negative     */
+  FA_ERR_ALIAS = 7,       /* o or lse overlaps q, k, v, or each other               */
+  FA_ERR_OVERFLOW = 8,    /* the problem exceeds the kernel's index or grid range   */
+  FA_ERR_HIP = 9          /* the HIP runtime refused a call; see fa_last_hip_error  */
+} fa_status;
+
+/*
+ * fa_forward -- O and LSE of exact scaled-dot-product attention.
+ *
+ *   q, k, v  [batch, heads, n, d_k] of `dtype` (read only)
+ *   o        [batch, heads, n, d_k] output (input type; bf16 for FP8_E4M3)
+ *   lse      [batch, heads, n] fp32 output, natural-log log-sum-exp of the
+ *            scaled (and masked) scores of each row; may be NULL (not written)
+ *   scale    multiplier of Q K^T (typically 1/sqrt(d_k))
+ *   causal   1: key j is excluded from query i when j > i; 0: no mask
+ *   dtype    an fa_dtype; FA_FP8_E4M3 here means all descales are 1.0
+ *   stream   hipStream_t to enqueue on (NULL: the null stream)
+ */
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+               int batch, int heads, int n, int d_k, float scale, int causal,
+               int dtype, void* stream);
+
+/*
+ * fa_forward_fp8 -- as fa_forward for FP8_E4M3 inputs with one fp32 descale
+ * per tensor: the value of an element is (its e4m3 code value) * descale.
+ * The scores are scale * q_descale * k_descale * (Q8 K8^T); O is
+ * v_descale * (P V8), written as bf16. LSE is in units of those scores.
+ * Descales must be finite and > 0. (FP8 is the input precision that the
+ * dictionary entry "FlashAttention" credits to FlashAttention-3.)
+ */
+int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int batch, int heads, int n, int d_k, float scale, int causal,
+                   float q_descale, float k_descale, float v_descale, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fa_status_string(int status);
+
+/* hipError_t of the most recent FA_ERR_HIP returned on the calling thread
+ * (0 if none). */
+int fa_last_hip_error(void);
+
+/* Version of this ABI: major * 10000 + minor * 100 + patch. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_FA_H */

@@ -1,0 +1,147 @@
+"""Python face of the fused attention forward library (``libfa.so``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of ``include/fa.h``. PyTorch supplies device memory
+and the current stream. There is no fallback: if the library is missing,
+importing works but every call raises.
+
+    o, lse = forward(q, k, v, causal=True)              # f32 / f16 / bf16
+    o, lse = forward_fp8(q8, k8, v8, qd, kd, vd)         # e4m3fn + descales
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+# fa_dtype (include/fa.h)
+FA_F32, FA_F16, FA_BF16, FA_FP8_E4M3 = 0, 1, 2, 3
+_DTYPE_CODE = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16,
+               torch.float8_e4m3fn: FA_FP8_E4M3}
+_OUT_DTYPE = {torch.float32: torch.float32, torch.float16: torch.float16,
+              torch.bfloat16: torch.bfloat16, torch.float8_e4m3fn: torch.bfloat16}
+
+# fa_status (include/fa.h)
+STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_DTYPE",
+          4: "FA_ERR_UNSUPPORTED", 5: "FA_ERR_ALIGN", 6: "FA_ERR_SCALE", 7: "FA_ERR_ALIAS",
+          8: "FA_ERR_OVERFLOW", 9: "FA_ERR_HIP"}
+
+EXPORTS = ("fa_forward", "fa_forward_fp8", "fa_status_string", "fa_last_hip_error",
+           "fa_abi_version")
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa.so (once) and declare its signatures. Raises if missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() "
+                           "(the HIP library is required, there is no fallback)")
+    lib = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_forward.restype = i
+    lib.fa_forward_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, f, f, f, vp]
+    lib.fa_forward_fp8.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_last_hip_error.argtypes = []
+    lib.fa_last_hip_error.restype = i
+    lib.fa_abi_version.argtypes = []
+    lib.fa_abi_version.restype = i
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        msg = lib.fa_status_string(status).decode()
+        if status == 9:
+            msg += f" (hipError_t {lib.fa_last_hip_error()})"
+        raise FAError(status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _prepare(q, k, v, out, lse):
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [batch, heads, n, d_k] shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    b, h, n, d = q.shape
+    if out is None:
+        out = torch.empty((b, h, n, d), dtype=_OUT_DTYPE[q.dtype], device=q.device)
+    if lse is None:
+        lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+    return out, lse
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+            scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, want_lse: bool = True
+            ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """O and LSE of softmax(scale * q k^T + mask) v via ``fa_forward``.
+
+    q, k, v: contiguous [batch, heads, n, d_k] device tensors (f32, f16 or
+    bf16; e4m3fn means all descales are 1). scale defaults to 1/sqrt(d_k).
+    Enqueued on torch's current stream; returns immediately.
+    """
+    lib = load_library()
+    out, lse = _prepare(q, k, v, out, lse if want_lse else None)
+    if not want_lse:
+        lse = None
+    b, h, n, d = q.shape
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib.fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, h, n, d, s,
+                        1 if causal else 0, _DTYPE_CODE[q.dtype], _stream(q.device))
+    _check(st)
+    return out, lse
+
+
+def forward_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_descale: float,
+                k_descale: float, v_descale: float, causal: bool = False,
+                scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """``fa_forward_fp8``: e4m3fn q, k, v with per-tensor fp32 descales; bf16 O."""
+    lib = load_library()
+    if q.dtype != torch.float8_e4m3fn:
+        raise ValueError("forward_fp8 takes float8_e4m3fn tensors")
+    out, lse = _prepare(q, k, v, out, lse)
+    b, h, n, d = q.shape
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib.fa_forward_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, h, n, d, s,
+                            1 if causal else 0, float(q_descale), float(k_descale),
+                            float(v_descale), _stream(q.device))
+    _check(st)
+    return out, lse

@@ -1,0 +1,138 @@
+// Host front end of the C ABI declared in include/fa.h: argument validation
+// (pure host code, before any HIP call), then one kernel launch.
+#include <cmath>
+#include <cstdint>
+#include <cfloat>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kAbiVersion = 10000;  // 1.0.0
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// The grid has one workgroup per (batch*head, 128-row query tile); its size
+// must fit gridDim.x. Element offsets inside the kernels are 64-bit.
+constexpr int64_t kMaxGrid = 0x7fffffff;
+constexpr double kLog2e = 1.4426950408889634;
+
+int validate(const void* q, const void* k, const void* v, void* o, const float* lse, int batch,
+             int heads, int n, int d_k, float scale, int causal, int dtype) {
+  if (!q || !k || !v || !o) return FA_ERR_NULL;
+  if (batch < 1 || heads < 1 || n < 1) return FA_ERR_SHAPE;
+  if (dtype < FA_F32 || dtype > FA_FP8_E4M3) return FA_ERR_DTYPE;
+  if ((d_k != 64 && d_k != 128) || (causal != 0 && causal != 1)) return FA_ERR_UNSUPPORTED;
+  const uintptr_t ptrs[5] = {(uintptr_t)q, (uintptr_t)k, (uintptr_t)v, (uintptr_t)o, (uintptr_t)lse};
+  for (uintptr_t p : ptrs)
+    if (p % 16) return FA_ERR_ALIGN;
+  if (!std::isfinite(scale) || scale < 0.f || !std::isfinite((float)(scale * kLog2e)))
+    return FA_ERR_SCALE;
+
+  const int64_t bh = (int64_t)batch * heads;
+  const int64_t rows = bh * n;
+  const int64_t tiles = ((int64_t)n + 127) / 128;
+  if (bh > kMaxGrid || bh * tiles > kMaxGrid) return FA_ERR_OVERFLOW;
+  const int in_bytes = dtype == FA_F32 ? 4 : dtype == FA_FP8_E4M3 ? 1 : 2;
+  const int out_bytes = dtype == FA_F32 ? 4 : 2;
+  // byte sizes must fit comfortably in 63 bits
+  if (rows > (INT64_C(1) << 62) / ((int64_t)d_k * 4)) return FA_ERR_OVERFLOW;
+  const int64_t in_sz = rows * d_k * in_bytes, out_sz = rows * d_k * out_bytes, lse_sz = rows * 4;
+
+  const Range rq{(uintptr_t)q, (uintptr_t)q + (uintptr_t)in_sz};
+  const Range rk{(uintptr_t)k, (uintptr_t)k + (uintptr_t)in_sz};
+  const Range rv{(uintptr_t)v, (uintptr_t)v + (uintptr_t)in_sz};
+  const Range ro{(uintptr_t)o, (uintptr_t)o + (uintptr_t)out_sz};
+  if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv)) return FA_ERR_ALIAS;
+  if (lse) {
+    const Range rl{(uintptr_t)lse, (uintptr_t)lse + (uintptr_t)lse_sz};
+    if (overlap(rl, rq) || overlap(rl, rk) || overlap(rl, rv) || overlap(rl, ro)) return FA_ERR_ALIAS;
+  }
+  return FA_OK;
+}
+
+int run(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int heads,
+        int n, int d_k, float qk_scale, int causal, int dtype, float o_mult, void* stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) {
+    fa::FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.bh = batch * heads;
+    a.n = n;
+    a.d = d_k;
+    a.causal = causal != 0;
+    // The kernels need c > 0: a zero scale is replaced by the smallest normal
+    // float, for which every exp2 argument rounds to 0 exactly as with c = 0
+    // (uniform weights), while masked scores (-inf) still give weight 0.
+    float c = (float)(qk_scale * kLog2e);
+    if (!(c > 0.f)) c = FLT_MIN;
+    a.c = c;
+    a.o_mult = o_mult;
+    a.elt = static_cast<fa::Elt>(dtype);
+    e = fa::launch_forward(a, static_cast<hipStream_t>(stream));
+  }
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+               int heads, int n, int d_k, float scale, int causal, int dtype, void* stream) {
+  const int st = validate(q, k, v, o, lse, batch, heads, n, d_k, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  return run(q, k, v, o, lse, batch, heads, n, d_k, scale, causal, dtype, 1.0f, stream);
+}
+
+int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                   int heads, int n, int d_k, float scale, int causal, float q_descale,
+                   float k_descale, float v_descale, void* stream) {
+  const int st = validate(q, k, v, o, lse, batch, heads, n, d_k, scale, causal, FA_FP8_E4M3);
+  if (st != FA_OK) return st;
+  for (float s : {q_descale, k_descale, v_descale})
+    if (!std::isfinite(s) || !(s > 0.f)) return FA_ERR_SCALE;
+  const float qk = (float)((double)scale * q_descale * k_descale);
+  if (!std::isfinite((float)(qk * kLog2e))) return FA_ERR_SCALE;
+  return run(q, k, v, o, lse, batch, heads, n, d_k, qk, causal, FA_FP8_E4M3, v_descale, stream);
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "null q, k, v or o pointer";
+    case FA_ERR_SHAPE: return "batch, heads and n must be >= 1";
+    case FA_ERR_DTYPE: return "unknown dtype";
+    case FA_ERR_UNSUPPORTED: return "unsupported d_k (64 or 128) or causal flag (0 or 1)";
+    case FA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case FA_ERR_SCALE: return "scale or descale not finite, or negative";
+    case FA_ERR_ALIAS: return "o or lse overlaps an input or each other";
+    case FA_ERR_OVERFLOW: return "problem exceeds the kernel's index or grid range";
+    case FA_ERR_HIP: return "HIP runtime error (see fa_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+int fa_last_hip_error(void) { return g_last_hip_error; }
+
+int fa_abi_version(void) { return kAbiVersion; }
+
+}  // extern "C"

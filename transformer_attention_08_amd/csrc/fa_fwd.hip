@@ -1,0 +1,573 @@
+// Fused attention forward pass for gfx950 (CDNA4, MI355X).
+//
+// One workgroup owns one tile of query rows of one (batch, head) and streams
+// every key/value tile it needs through LDS, merging tiles with the online
+// softmax of the slides "Case study: FlashAttention" (slide "Online softmax:
+// divide once, at the end"): running max m, running sum l, unnormalised
+// output o, rescale alpha = e^(m_old - m_new), and one division by l per row
+// at the end. Neither the score tile S nor the probability tile P leaves the
+// registers (slide "FlashAttention: the idea": tiling plus fusion, S and P
+// never stored).
+//
+// Register layout (the central design choice). Each wave owns 32 query rows.
+// It computes the transposed score tile S^T = K Q^T with the 32x32 MFMA, so
+// the MFMA accumulator puts one query on each lane (lane % 32) and 16 keys
+// in that lane's registers; the other 16 keys of the 32-key block sit in the
+// partner lane (lane ^ 32). Consequences:
+//   * the row max and row sum are reductions over a lane's own registers
+//     plus one exchange with lane ^ 32;
+//   * the accumulator registers, packed to 16 bits, are directly the B
+//     operand of the second MFMA O^T = V^T P^T, which again has the query on
+//     the lane, so the per-row rescale alpha is a lane-local multiply;
+//   * keys are assigned to accumulator rows by a fixed permutation (bits 2
+//     and 3 of the row index swapped) so that the 8 keys a lane feeds into
+//     one P.V MFMA step are 8 consecutive keys. A sum over keys does not
+//     depend on their order, so only the K and V tile reads need to agree.
+// V is transposed once per tile while it is written to LDS, so that the A
+// operand of O^T = V^T P^T is one 16-byte LDS read per lane.
+//
+// Scale. The exponentials are exp2 with c = scale * log2(e) folded into the
+// score ("Mastering FlashAttention: The Algebraic Foundation", key points:
+// the qk_scale constant log2(e)/sqrt(D)). The running max is kept in those
+// base-2 units; LSE is converted back to natural-log units at the end.
+//
+// Work decomposition. The grid has one workgroup per (batch*head, query
+// tile). Causal launches visit the longest query tiles first. When the
+// number of (batch, head) pairs is a multiple of 8, the workgroups of each
+// head are mapped onto one XCD (workgroups are dispatched round-robin over
+// the 8 XCDs), so the K/V tiles of a head are re-read from that XCD's L2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_kernels.h"
+
+namespace fa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBq = 32 * kWaves;  // query rows per workgroup
+constexpr float kLn2 = 0.693147180559945309f;
+
+struct TileId {
+  int bh;
+  int t;
+};
+
+// Workgroup id -> (batch*head, query tile).
+__device__ inline TileId tile_of_block(int pid, int bh_count, int tiles, bool causal) {
+  int bh, tt;
+  if ((bh_count & 7) == 0) {
+    const int xcd = pid & 7, slot = pid >> 3, per = bh_count >> 3;
+    tt = slot / per;
+    bh = xcd * per + slot % per;
+  } else {
+    tt = pid / bh_count;
+    bh = pid % bh_count;
+  }
+  return {bh, causal ? tiles - 1 - tt : tt};
+}
+
+// Accumulator row m of S^T holds key perm32(m) of the 32-key block.
+__device__ inline int perm32(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <Elt E>
+__device__ inline uint32_t pack2(float a, float b) {
+  if constexpr (E == Elt::F16) {
+    f16x2_t h = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, h);
+  } else {
+    bf16x2_t h = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, h);
+  }
+}
+
+// o += a * b on the 32x32x16 MFMA with 16-bit operands (F16 or BF16).
+template <Elt E>
+__device__ inline f32x16_t mfma16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  if constexpr (E == Elt::F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ inline f32x16_t mfma_fp8(u32x2_t a, u32x2_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(__builtin_bit_cast(long, a),
+                                                     __builtin_bit_cast(long, b), c, 0, 0, 0);
+}
+
+// Two OCP e4m3 codes (bytes 0,1 or, with HI, bytes 2,3 of w) -> two bf16,
+// exactly (every e4m3 value is a bf16 value).
+template <bool HI>
+__device__ inline uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  bf16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// ---------------------------------------------------------------------------
+// 16-bit and fp8 kernel. IN: element type of q/k/v. P.V runs on the 16-bit
+// MFMA (f16 for F16 input, bf16 otherwise; fp8 V is widened exactly to bf16
+// while it is transposed into LDS).
+// ---------------------------------------------------------------------------
+template <Elt IN, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_mfma16(FwdArgs a) {
+  constexpr bool F8 = IN == Elt::FP8;
+  constexpr Elt PE = IN == Elt::F16 ? Elt::F16 : Elt::BF16;  // P, V^T and O element type
+  constexpr int QB = F8 ? 1 : 2;       // bytes per q/k/v element
+  constexpr int BK = 64;               // keys per tile
+  constexpr int KS = D + 8;            // K row stride in LDS, elements
+  constexpr int VS = BK + 8;           // V^T row stride in LDS, 16-bit elements
+  constexpr int K_BYTES = BK * KS * QB;
+  constexpr int V_BYTES = D * VS * 2;
+  constexpr int STAGE = K_BYTES + V_BYTES;
+  constexpr int CH = 16 / QB;          // elements per 16-byte global chunk
+  constexpr int CPR = D / CH;          // chunks per row
+  constexpr int NLD = BK * CPR / kThreads;  // chunks per thread per tile (K and V alike)
+  constexpr int VGRP = BK / NLD;       // V row groups per tile
+  constexpr int NKS = D / 16;          // MFMA k-steps of Q K^T
+  constexpr int NDB = D / 32;          // 32-column blocks of O
+  static_assert(NLD >= 1 && NLD <= 4 && CPR * VGRP == kThreads, "tile mapping");
+  static_assert(K_BYTES % 16 == 0 && STAGE % 16 == 0, "LDS alignment");
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, lr = lane & 31, hl = lane >> 5;
+  const int n = a.n;
+  const int tiles = (n + kBq - 1) / kBq;
+  const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
+  const int q0 = tl.t * kBq;
+  const int qw0 = q0 + 32 * w;        // first query row of this wave
+  const int qrow = qw0 + lr;          // query row of this lane
+  const size_t head_off = (size_t)tl.bh * (size_t)n * D;
+
+  const uint8_t* Qg = (const uint8_t*)a.q + head_off * QB;
+  const u32x4_t* Kg = (const u32x4_t*)((const uint8_t*)a.k + head_off * QB);
+  const u32x4_t* Vg = (const u32x4_t*)((const uint8_t*)a.v + head_off * QB);
+
+  // Q fragments (B operand of S^T = K Q^T): lane holds query qrow, d-columns
+  // ks*16 + hl*8 .. +8 for each k-step ks.
+  u32x4_t qf[F8 ? 1 : NKS];
+  u32x2_t qf8[F8 ? NKS : 1];
+  {
+    const bool ok = qrow < n;
+    const uint8_t* qp = Qg + (size_t)(ok ? qrow : 0) * D * QB;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if constexpr (F8) {
+        u32x2_t x = *(const u32x2_t*)(qp + ks * 16 + hl * 8);
+        qf8[ks] = ok ? x : u32x2_t{0, 0};
+      } else {
+        u32x4_t x = *(const u32x4_t*)(qp + (ks * 16 + hl * 8) * 2);
+        qf[ks] = ok ? x : u32x4_t{0, 0, 0, 0};
+      }
+    }
+  }
+
+  int nt;
+  if (CAUSAL) {
+    const int last = min(q0 + kBq, n) - 1;
+    nt = last / BK + 1;
+  } else {
+    nt = (n + BK - 1) / BK;
+  }
+
+  // Register staging of the next tile's global loads.
+  u32x4_t kreg[NLD], vreg[NLD];
+  const int vgrp = tid % VGRP, vch = tid / VGRP;  // V: rows NLD*vgrp.., chunk vch
+
+  auto gload = [&](int j) {
+    const int key0 = j * BK;
+#pragma unroll
+    for (int it = 0; it < NLD; ++it) {
+      const int idx = tid + it * kThreads;
+      const int row = idx / CPR, c = idx % CPR;
+      const int key = key0 + row;
+      kreg[it] = key < n ? Kg[(size_t)key * CPR + c] : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int r = 0; r < NLD; ++r) {
+      const int key = key0 + NLD * vgrp + r;
+      vreg[r] = key < n ? Vg[(size_t)key * CPR + vch] : u32x4_t{0, 0, 0, 0};
+    }
+  };
+
+  auto swrite = [&](int buf) {
+    uint8_t* kl = smem + buf * STAGE;
+#pragma unroll
+    for (int it = 0; it < NLD; ++it) {
+      const int idx = tid + it * kThreads;
+      const int row = idx / CPR, c = idx % CPR;
+      uint8_t* dst = kl + (row * KS + c * CH) * QB;
+      if constexpr (F8) {
+        *(u32x2_t*)dst = u32x2_t{kreg[it][0], kreg[it][1]};
+        *(u32x2_t*)(dst + 8) = u32x2_t{kreg[it][2], kreg[it][3]};
+      } else {
+        *(u32x4_t*)dst = kreg[it];
+      }
+    }
+    // V^T: row d, keys contiguous. vw[r][i] holds 16-bit elements 2i, 2i+1
+    // of this thread's chunk of key row NLD*vgrp + r.
+    uint32_t vw[NLD][CH / 2];
+#pragma unroll
+    for (int r = 0; r < NLD; ++r) {
+#pragma unroll
+      for (int i = 0; i < CH / 2; ++i) {
+        if constexpr (F8)
+          vw[r][i] = (i & 1) ? e4m3x2_to_bf16x2<true>(vreg[r][i / 2])
+                             : e4m3x2_to_bf16x2<false>(vreg[r][i / 2]);
+        else
+          vw[r][i] = vreg[r][i];
+      }
+    }
+    uint16_t* vt = (uint16_t*)(kl + K_BYTES);
+#pragma unroll
+    for (int dd = 0; dd < CH; ++dd) {
+      uint16_t* dst = vt + (vch * CH + dd) * VS + NLD * vgrp;
+      const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
+      if constexpr (NLD == 4) {
+        const uint32_t x0 = __builtin_amdgcn_perm(vw[1][dd / 2], vw[0][dd / 2], sel);
+        const uint32_t x1 = __builtin_amdgcn_perm(vw[3][dd / 2], vw[2][dd / 2], sel);
+        *(u32x2_t*)dst = u32x2_t{x0, x1};
+      } else if constexpr (NLD == 2) {
+        *(uint32_t*)dst = __builtin_amdgcn_perm(vw[1][dd / 2], vw[0][dd / 2], sel);
+      } else {
+        *dst = (uint16_t)((dd & 1) ? (vw[0][dd / 2] >> 16) : (vw[0][dd / 2] & 0xffffu));
+      }
+    }
+  };
+
+  float m2 = -INFINITY;  // running max of c * s (base-2 units)
+  float lp = 0.f;        // this lane's part of the running sum l
+  f32x16_t o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = f32x16_t{};
+
+  const float c = a.c;
+  const bool wave_live = qw0 < n;
+  const int krow = perm32(lr);
+
+  gload(0);
+  swrite(0);
+  __syncthreads();
+
+  for (int j = 0; j < nt; ++j) {
+    if (j + 1 < nt) gload(j + 1);
+    const int kbase = j * BK;
+    const bool skip = !wave_live || (CAUSAL && kbase > qw0 + 31);
+    if (!skip) {
+      const uint8_t* kl = smem + (j & 1) * STAGE;
+      const uint16_t* vt = (const uint16_t*)(kl + K_BYTES);
+
+      // S^T = K Q^T for the two 32-key blocks of the tile.
+      f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int row = kb * 32 + krow;
+          if constexpr (F8) {
+            const u32x2_t av = *(const u32x2_t*)(kl + row * KS + ks * 16 + hl * 8);
+            s[kb] = mfma_fp8(av, qf8[ks], s[kb]);
+          } else {
+            const u32x4_t av = *(const u32x4_t*)(kl + (row * KS + ks * 16 + hl * 8) * 2);
+            s[kb] = mfma16<IN>(av, qf[ks], s[kb]);
+          }
+        }
+      }
+
+      // Mask: keys past the end, and (causal) keys after the query.
+      const bool need_mask = (kbase + BK > n) || (CAUSAL && kbase + BK - 1 > qw0);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kbase + kb * 32 + 16 * (i >> 3) + 8 * hl + (i & 7);
+            const bool ok = key < n && (!CAUSAL || key <= qrow);
+            s[kb][i] = ok ? s[kb][i] : -INFINITY;
+          }
+        }
+      }
+
+      // Online softmax update for this lane's query row.
+      float mx = s[0][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m2, mx * c);
+      const float alpha = fast_exp2(m2 - m_new);
+      const float nm = -m_new;
+      float ls = 0.f;
+      u32x4_t pb[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const float p0 = fast_exp2(__builtin_fmaf(s[kb][i], c, nm));
+          const float p1 = fast_exp2(__builtin_fmaf(s[kb][i + 1], c, nm));
+          ls += p0 + p1;
+          pb[kb][i >> 3][(i & 7) >> 1] = pack2<PE>(p0, p1);
+        }
+      }
+      lp = __builtin_fmaf(alpha, lp, ls);
+      m2 = m_new;
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+      }
+
+      // O^T += V^T P^T: A = V^T rows (d), B = this lane's packed P.
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const u32x4_t av = *(const u32x4_t*)(vt + (db * 32 + lr) * VS + kb * 32 + 16 * s2 + 8 * hl);
+            o[db] = mfma16<PE>(av, pb[kb][s2], o[db]);
+          }
+        }
+      }
+    }
+    if (j + 1 < nt) swrite((j + 1) & 1);
+    __syncthreads();
+  }
+
+  // Epilogue: O = o / l once per row; LSE = ln 2 * (m2 + log2 l).
+  const float lt = lp + __shfl_xor(lp, 32);
+  if (qrow < n) {
+    const float inv = a.o_mult / lt;
+    uint16_t* Og = (uint16_t*)a.o + head_off + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + 8 * g + 4 * hl;
+        const uint32_t x0 = pack2<PE>(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+        const uint32_t x1 = pack2<PE>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+        *(u32x2_t*)(Og + d) = u32x2_t{x0, x1};
+      }
+    }
+    if (hl == 0 && a.lse) a.lse[(size_t)tl.bh * n + qrow] = (m2 + __log2f(lt)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel (32x32x2 fp32 MFMA, 32-key tiles). Same structure and register
+// layout as above; with one element per operand lane the P.V step reads V
+// rows straight from a row-major LDS tile, so no transpose is needed.
+// The k index of the Q K^T MFMA maps lane half hl, step ks to column
+// hl * D/2 + ks, so both operands are read as contiguous 16-byte runs.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd_mfma32(FwdArgs a) {
+  constexpr int BK = 32;
+  constexpr int KS = D + 4;   // K row stride (floats): 16-byte reads of 16 rows hit distinct banks
+  constexpr int VS = D + 8;   // V row stride (floats): rows r and r+4 fall in opposite bank halves
+  constexpr int K_FL = BK * KS, V_FL = BK * VS, STAGE = K_FL + V_FL;
+  constexpr int CPR = D / 4;                 // 16-byte chunks per row
+  constexpr int NLD = BK * CPR / kThreads;   // chunks per thread per tile (2 or 4)
+  constexpr int HALF = D / 2;
+  constexpr int NDB = D / 32;
+
+  __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, lr = lane & 31, hl = lane >> 5;
+  const int n = a.n;
+  const int tiles = (n + kBq - 1) / kBq;
+  const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
+  const int q0 = tl.t * kBq;
+  const int qw0 = q0 + 32 * w;
+  const int qrow = qw0 + lr;
+  const size_t head_off = (size_t)tl.bh * (size_t)n * D;
+  const float* Qg = (const float*)a.q + head_off;
+  const u32x4_t* Kg = (const u32x4_t*)((const float*)a.k + head_off);
+  const u32x4_t* Vg = (const u32x4_t*)((const float*)a.v + head_off);
+
+  float qf[HALF];
+  {
+    const bool ok = qrow < n;
+    const u32x4_t* qp = (const u32x4_t*)(Qg + (size_t)(ok ? qrow : 0) * D + hl * HALF);
+#pragma unroll
+    for (int i = 0; i < HALF / 4; ++i) {
+      u32x4_t x = qp[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qf[4 * i + e] = ok ? __uint_as_float(x[e]) : 0.f;
+    }
+  }
+
+  int nt;
+  if (CAUSAL) {
+    const int last = min(q0 + kBq, n) - 1;
+    nt = last / BK + 1;
+  } else {
+    nt = (n + BK - 1) / BK;
+  }
+
+  u32x4_t kreg[NLD], vreg[NLD];
+  auto gload = [&](int j) {
+    const int key0 = j * BK;
+#pragma unroll
+    for (int it = 0; it < NLD; ++it) {
+      const int idx = tid + it * kThreads;
+      const int row = idx / CPR, ch = idx % CPR;
+      const int key = key0 + row;
+      const bool ok = key < n;
+      kreg[it] = ok ? Kg[(size_t)key * CPR + ch] : u32x4_t{0, 0, 0, 0};
+      vreg[it] = ok ? Vg[(size_t)key * CPR + ch] : u32x4_t{0, 0, 0, 0};
+    }
+  };
+  auto swrite = [&](int buf) {
+    float* kl = smem + buf * STAGE;
+#pragma unroll
+    for (int it = 0; it < NLD; ++it) {
+      const int idx = tid + it * kThreads;
+      const int row = idx / CPR, ch = idx % CPR;
+      *(u32x4_t*)(kl + row * KS + ch * 4) = kreg[it];
+      *(u32x4_t*)(kl + K_FL + row * VS + ch * 4) = vreg[it];
+    }
+  };
+
+  float m2 = -INFINITY, lp = 0.f;
+  f32x16_t o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = f32x16_t{};
+  const float c = a.c;
+  const bool wave_live = qw0 < n;
+
+  gload(0);
+  swrite(0);
+  __syncthreads();
+
+  for (int j = 0; j < nt; ++j) {
+    if (j + 1 < nt) gload(j + 1);
+    const int kbase = j * BK;
+    const bool skip = !wave_live || (CAUSAL && kbase > qw0 + 31);
+    if (!skip) {
+      const float* kl = smem + (j & 1) * STAGE;
+      const float* vl = kl + K_FL;
+      f32x16_t s = f32x16_t{};
+      const float* kr = kl + lr * KS + hl * HALF;
+#pragma unroll
+      for (int i = 0; i < HALF / 4; ++i) {
+        const u32x4_t kv = *(const u32x4_t*)(kr + 4 * i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(kv[e]), qf[4 * i + e], s, 0, 0, 0);
+      }
+      // accumulator register i of lane half hl holds key 8(i/4) + 4 hl + i%4
+      const bool need_mask = (kbase + BK > n) || (CAUSAL && kbase + BK - 1 > qw0);
+      if (need_mask) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kbase + 8 * (i >> 2) + 4 * hl + (i & 3);
+          const bool ok = key < n && (!CAUSAL || key <= qrow);
+          s[i] = ok ? s[i] : -INFINITY;
+        }
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m2, mx * c);
+      const float alpha = fast_exp2(m2 - m_new);
+      const float nm = -m_new;
+      float ls = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[i] = fast_exp2(__builtin_fmaf(s[i], c, nm));
+        ls += s[i];
+      }
+      lp = __builtin_fmaf(alpha, lp, ls);
+      m2 = m_new;
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = 8 * (i >> 2) + 4 * hl + (i & 3);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vl[key * VS + db * 32 + lr], s[i], o[db], 0, 0, 0);
+        }
+      }
+    }
+    if (j + 1 < nt) swrite((j + 1) & 1);
+    __syncthreads();
+  }
+
+  const float lt = lp + __shfl_xor(lp, 32);
+  if (qrow < n) {
+    const float inv = a.o_mult / lt;
+    float* Og = (float*)a.o + head_off + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + 8 * g + 4 * hl;
+        u32x4_t x;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = __float_as_uint(o[db][4 * g + r] * inv);
+        *(u32x4_t*)(Og + d) = x;
+      }
+    }
+    if (hl == 0 && a.lse) a.lse[(size_t)tl.bh * n + qrow] = (m2 + __log2f(lt)) * kLn2;
+  }
+}
+
+template <typename K>
+hipError_t launch(K kernel, const FwdArgs& a, hipStream_t stream) {
+  const int tiles = (a.n + kBq - 1) / kBq;
+  const unsigned grid = (unsigned)a.bh * (unsigned)tiles;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <Elt E, int D>
+hipError_t dispatch_causal(const FwdArgs& a, hipStream_t s) {
+  if constexpr (E == Elt::F32) {
+    return a.causal ? launch(fwd_mfma32<D, true>, a, s) : launch(fwd_mfma32<D, false>, a, s);
+  } else {
+    return a.causal ? launch(fwd_mfma16<E, D, true>, a, s) : launch(fwd_mfma16<E, D, false>, a, s);
+  }
+}
+
+template <Elt E>
+hipError_t dispatch_d(const FwdArgs& a, hipStream_t s) {
+  return a.d == 64 ? dispatch_causal<E, 64>(a, s) : dispatch_causal<E, 128>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_forward(const FwdArgs& a, hipStream_t stream) {
+  switch (a.elt) {
+    case Elt::F32: return dispatch_d<Elt::F32>(a, stream);
+    case Elt::F16: return dispatch_d<Elt::F16>(a, stream);
+    case Elt::BF16: return dispatch_d<Elt::BF16>(a, stream);
+    case Elt::FP8: return dispatch_d<Elt::FP8>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa
