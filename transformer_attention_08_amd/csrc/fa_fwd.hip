@@ -39,6 +39,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_kernels.h"
 
 namespace fa {
@@ -120,19 +122,72 @@ __device__ inline uint32_t e4m3x2_to_bf16x2(uint32_t w) {
 // the fp8 MFMA sums its products with about 3e-5 relative error, which at
 // scores near 100 puts the log-sum-exp off by more than 1e-3, while the bf16
 // MFMA accumulates these same exact products in full fp32 precision.
+//
+// Pipeline. Iteration j applies the softmax to the scores of key tile j
+// (computed one iteration earlier) while the MFMA pipe already computes the
+// scores of tile j+1, then accumulates P_j V_j. K therefore runs one tile
+// ahead of V through the two LDS slots of each: during iteration j the waves
+// read K_{j+1} and V_j and the staged K_{j+2} and V_{j+1} are written into
+// the other slots, so one barrier per iteration suffices.
+//
+// Lazy rescale. The reference max m of a row only moves when a tile's max
+// exceeds it by more than kLazy (log2 units), so p <= 2^kLazy and o and l
+// are rescaled rarely. The result is unchanged: m cancels in o / l, and the
+// log-sum-exp is m + log2(l) for whatever m was used.
 // ---------------------------------------------------------------------------
+constexpr float kLazy = 8.0f;
+
+// Keys per K/V tile of the 16-bit kernel (32 or 64) and its waves per SIMD.
+#ifndef FA_TILE_KEYS
+#define FA_TILE_KEYS 32
+#endif
+#ifndef FA_WAVES_PER_SIMD
+#define FA_WAVES_PER_SIMD 2
+#endif
+
+// x of this lane and of lane ^ 32, in an order that is the same on both lanes.
+struct PairVals {
+  float a, b;
+};
+__device__ inline PairVals pair_vals(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ inline float pair_max(float x) {
+  const PairVals p = pair_vals(x);
+  return fmaxf(p.a, p.b);
+}
+__device__ inline float pair_sum(float x) {
+  const PairVals p = pair_vals(x);
+  return p.a + p.b;
+}
+
+// Buffer resource over [base, base + bytes): loads at offsets past the end
+// return zeros, which pads ragged tiles without branches.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ inline u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ inline u32x2_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
 template <Elt IN, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(FA_WAVES_PER_SIMD, FA_WAVES_PER_SIMD)))
 void fwd_mfma16(FwdArgs a) {
   constexpr bool F8 = IN == Elt::FP8;
   constexpr Elt PE = IN == Elt::F16 ? Elt::F16 : Elt::BF16;  // MFMA / LDS / O element type
   constexpr int GB = F8 ? 1 : 2;       // bytes per q/k/v element in global memory
-  constexpr int BK = 64;               // keys per tile
+  // keys per tile (fp8 with d_k 64 needs 64 keys to give every thread a chunk)
+  constexpr int BK = (F8 && D == 64) ? 64 : FA_TILE_KEYS;
+  constexpr int KB = BK / 32;          // 32-key blocks per tile
   constexpr int KS = D + 8;            // K row stride in LDS, 16-bit elements
   constexpr int VS = BK + 8;           // V^T row stride in LDS, 16-bit elements
   constexpr int K_BYTES = BK * KS * 2;
   constexpr int V_BYTES = D * VS * 2;
-  constexpr int STAGE = K_BYTES + V_BYTES;
   constexpr int CH = 16 / GB;          // elements per 16-byte global chunk
   constexpr int CPR = D / CH;          // chunks per row
   constexpr int NLD = BK * CPR / kThreads;  // chunks per thread per tile (K and V alike)
@@ -140,9 +195,12 @@ void fwd_mfma16(FwdArgs a) {
   constexpr int NKS = D / 16;          // MFMA k-steps of Q K^T
   constexpr int NDB = D / 32;          // 32-column blocks of O
   static_assert(NLD >= 1 && NLD <= 4 && CPR * VGRP == kThreads, "tile mapping");
-  static_assert(K_BYTES % 16 == 0 && STAGE % 16 == 0, "LDS alignment");
+  static_assert(K_BYTES % 16 == 0 && V_BYTES % 16 == 0, "LDS alignment");
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  // [K slot 0][K slot 1][V^T slot 0][V^T slot 1]
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * K_BYTES + 2 * V_BYTES];
+  uint8_t* const kls = smem;
+  uint8_t* const vls = smem + 2 * K_BYTES;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 31, hl = lane >> 5;
@@ -153,28 +211,24 @@ void fwd_mfma16(FwdArgs a) {
   const int qw0 = q0 + 32 * w;        // first query row of this wave
   const int qrow = qw0 + lr;          // query row of this lane
   const size_t head_off = (size_t)tl.bh * (size_t)n * D;
+  const uint32_t head_bytes = (uint32_t)n * D * GB;
 
-  const uint8_t* Qg = (const uint8_t*)a.q + head_off * GB;
-  const u32x4_t* Kg = (const u32x4_t*)((const uint8_t*)a.k + head_off * GB);
-  const u32x4_t* Vg = (const u32x4_t*)((const uint8_t*)a.v + head_off * GB);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint8_t*)a.q + head_off * GB, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint8_t*)a.k + head_off * GB, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint8_t*)a.v + head_off * GB, head_bytes);
 
   // Q fragments (B operand of S^T = K Q^T): lane holds query qrow, d-columns
-  // ks*16 + hl*8 .. +8 for each k-step ks.
+  // ks*16 + hl*8 .. +8 for each k-step ks. Rows past n load as zeros.
   u32x4_t qf[NKS];
-  {
-    const bool ok = qrow < n;
-    const uint8_t* qp = Qg + (size_t)(ok ? qrow : 0) * D * GB;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      u32x4_t x;
-      if constexpr (F8) {
-        const u32x2_t b = *(const u32x2_t*)(qp + ks * 16 + hl * 8);
-        x = u32x4_t{e4m3x2_to_bf16x2<false>(b[0]), e4m3x2_to_bf16x2<true>(b[0]),
-                    e4m3x2_to_bf16x2<false>(b[1]), e4m3x2_to_bf16x2<true>(b[1])};
-      } else {
-        x = *(const u32x4_t*)(qp + (ks * 16 + hl * 8) * 2);
-      }
-      qf[ks] = ok ? x : u32x4_t{0, 0, 0, 0};
+  for (int ks = 0; ks < NKS; ++ks) {
+    const uint32_t off = ((uint32_t)qrow * D + ks * 16 + hl * 8) * GB;
+    if constexpr (F8) {
+      const u32x2_t b = bload8(rq, off);
+      qf[ks] = u32x4_t{e4m3x2_to_bf16x2<false>(b[0]), e4m3x2_to_bf16x2<true>(b[0]),
+                       e4m3x2_to_bf16x2<false>(b[1]), e4m3x2_to_bf16x2<true>(b[1])};
+    } else {
+      qf[ks] = bload16(rq, off);
     }
   }
 
@@ -186,43 +240,44 @@ void fwd_mfma16(FwdArgs a) {
     nt = (n + BK - 1) / BK;
   }
 
-  // Register staging of the next tile's global loads.
-  u32x4_t kreg[NLD], vreg[NLD];
+  // ---- staging of global tiles through registers
+  u32x4_t kst[NLD], vst[NLD];
   const int vgrp = tid % VGRP, vch = tid / VGRP;  // V: rows NLD*vgrp.., chunk vch
 
-  auto gload = [&](int j) {
-    const int key0 = j * BK;
+  auto load_k = [&](int j) {
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
       const int idx = tid + it * kThreads;
       const int row = idx / CPR, c = idx % CPR;
-      const int key = key0 + row;
-      kreg[it] = key < n ? Kg[(size_t)key * CPR + c] : u32x4_t{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int r = 0; r < NLD; ++r) {
-      const int key = key0 + NLD * vgrp + r;
-      vreg[r] = key < n ? Vg[(size_t)key * CPR + vch] : u32x4_t{0, 0, 0, 0};
+      kst[it] = bload16(rk, ((uint32_t)(j * BK + row) * CPR + c) * 16);
     }
   };
-
-  auto swrite = [&](int buf) {
-    uint8_t* kl = smem + buf * STAGE;
+  auto load_v = [&](int j) {
+#pragma unroll
+    for (int r = 0; r < NLD; ++r) {
+      const int key = j * BK + NLD * vgrp + r;
+      vst[r] = bload16(rv, ((uint32_t)key * CPR + vch) * 16);
+    }
+  };
+  auto store_k = [&](int slot) {
+    uint8_t* kl = kls + slot * K_BYTES;
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
       const int idx = tid + it * kThreads;
       const int row = idx / CPR, c = idx % CPR;
       uint8_t* dst = kl + (row * KS + c * CH) * 2;
       if constexpr (F8) {
-        const u32x4_t x = kreg[it];
+        const u32x4_t x = kst[it];
         *(u32x4_t*)dst = u32x4_t{e4m3x2_to_bf16x2<false>(x[0]), e4m3x2_to_bf16x2<true>(x[0]),
                                  e4m3x2_to_bf16x2<false>(x[1]), e4m3x2_to_bf16x2<true>(x[1])};
         *(u32x4_t*)(dst + 16) = u32x4_t{e4m3x2_to_bf16x2<false>(x[2]), e4m3x2_to_bf16x2<true>(x[2]),
                                         e4m3x2_to_bf16x2<false>(x[3]), e4m3x2_to_bf16x2<true>(x[3])};
       } else {
-        *(u32x4_t*)dst = kreg[it];
+        *(u32x4_t*)dst = kst[it];
       }
     }
+  };
+  auto store_v = [&](int slot) {
     // V^T: row d, keys contiguous. vw[r][i] holds 16-bit elements 2i, 2i+1
     // of this thread's chunk of key row NLD*vgrp + r.
     uint32_t vw[NLD][CH / 2];
@@ -231,13 +286,13 @@ void fwd_mfma16(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < CH / 2; ++i) {
         if constexpr (F8)
-          vw[r][i] = (i & 1) ? e4m3x2_to_bf16x2<true>(vreg[r][i / 2])
-                             : e4m3x2_to_bf16x2<false>(vreg[r][i / 2]);
+          vw[r][i] = (i & 1) ? e4m3x2_to_bf16x2<true>(vst[r][i / 2])
+                             : e4m3x2_to_bf16x2<false>(vst[r][i / 2]);
         else
-          vw[r][i] = vreg[r][i];
+          vw[r][i] = vst[r][i];
       }
     }
-    uint16_t* vt = (uint16_t*)(kl + K_BYTES);
+    uint16_t* vt = (uint16_t*)(vls + slot * V_BYTES);
 #pragma unroll
     for (int dd = 0; dd < CH; ++dd) {
       uint16_t* dst = vt + (vch * CH + dd) * VS + NLD * vgrp;
@@ -254,102 +309,137 @@ void fwd_mfma16(FwdArgs a) {
     }
   };
 
-  float m2 = -INFINITY;  // running max of c * s (base-2 units)
+  // ---- the two MFMA stages and the softmax
+  const int krow = perm32(lr);
+  auto scores = [&](int slot, f32x16_t (&s)[KB]) {
+    const uint8_t* kl = kls + slot * K_BYTES;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4_t av = *(const u32x4_t*)(kl + ((kb * 32 + krow) * KS + ks * 16 + hl * 8) * 2);
+        s[kb] = mfma16<PE>(av, qf[ks], s[kb]);
+      }
+    }
+  };
+
+  const float c = a.c;
+  float m2 = -INFINITY;  // reference max of c * s (base-2 units) for this row
   float lp = 0.f;        // this lane's part of the running sum l
   f32x16_t o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x16_t{};
 
-  const float c = a.c;
-  const bool wave_live = qw0 < n;
-  const int krow = perm32(lr);
-
-  gload(0);
-  swrite(0);
-  __syncthreads();
-
-  for (int j = 0; j < nt; ++j) {
-    if (j + 1 < nt) gload(j + 1);
-    const int kbase = j * BK;
-    const bool skip = !wave_live || (CAUSAL && kbase > qw0 + 31);
-    if (!skip) {
-      const uint8_t* kl = smem + (j & 1) * STAGE;
-      const uint16_t* vt = (const uint16_t*)(kl + K_BYTES);
-
-      // S^T = K Q^T for the two 32-key blocks of the tile.
-      f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+  // Softmax of one score tile into packed P, with the lazy rescale of o, l.
+  auto softmax = [&](f32x16_t (&s)[KB], u32x4_t (&pb)[KB][2]) {
+    float mx = s[0][0];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int row = kb * 32 + krow;
-          const u32x4_t av = *(const u32x4_t*)(kl + (row * KS + ks * 16 + hl * 8) * 2);
-          s[kb] = mfma16<PE>(av, qf[ks], s[kb]);
-        }
+    for (int kb = 1; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = pair_max(mx);
+    const float mc = mx * c;
+    const bool up = mc > m2 + kLazy;
+    const float m_use = up ? mc : m2;
+    const float alpha = fast_exp2(m2 - m_use);
+    const float nm = -m_use;
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[kb][i], c, nm));
+        const float p1 = fast_exp2(__builtin_fmaf(s[kb][i + 1], c, nm));
+        ls += p0 + p1;
+        pb[kb][i >> 3][(i & 7) >> 1] = pack2<PE>(p0, p1);
       }
+    }
+    lp = __builtin_fmaf(alpha, lp, ls);
+    m2 = m_use;
+    if (__any(up)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+    }
+  };
 
-      // Mask: keys past the end, and (causal) keys after the query.
-      const bool need_mask = (kbase + BK > n) || (CAUSAL && kbase + BK - 1 > qw0);
-      if (need_mask) {
+  auto mask = [&](f32x16_t (&s)[KB], int kbase) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kbase + kb * 32 + 16 * (i >> 3) + 8 * hl + (i & 7);
-            const bool ok = key < n && (!CAUSAL || key <= qrow);
-            s[kb][i] = ok ? s[kb][i] : -INFINITY;
-          }
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int key = kbase + kb * 32 + 16 * (i >> 3) + 8 * hl + (i & 7);
+        const bool ok = key < n && (!CAUSAL || key <= qrow);
+        s[kb][i] = ok ? s[kb][i] : -INFINITY;
       }
+    }
+  };
 
-      // Online softmax update for this lane's query row.
-      float mx = s[0][0];
+  auto pv = [&](int slot, const u32x4_t (&pb)[KB][2]) {
+    const uint16_t* vt = (const uint16_t*)(vls + slot * V_BYTES);
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+    for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m2, mx * c);
-      const float alpha = fast_exp2(m2 - m_new);
-      const float nm = -m_new;
-      float ls = 0.f;
-      u32x4_t pb[2][2];
+      for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const float p0 = fast_exp2(__builtin_fmaf(s[kb][i], c, nm));
-          const float p1 = fast_exp2(__builtin_fmaf(s[kb][i + 1], c, nm));
-          ls += p0 + p1;
-          pb[kb][i >> 3][(i & 7) >> 1] = pack2<PE>(p0, p1);
-        }
-      }
-      lp = __builtin_fmaf(alpha, lp, ls);
-      m2 = m_new;
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-      }
-
-      // O^T += V^T P^T: A = V^T rows (d), B = this lane's packed P.
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const u32x4_t av = *(const u32x4_t*)(vt + (db * 32 + lr) * VS + kb * 32 + 16 * s2 + 8 * hl);
-            o[db] = mfma16<PE>(av, pb[kb][s2], o[db]);
-          }
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const u32x4_t av = *(const u32x4_t*)(vt + (db * 32 + lr) * VS + kb * 32 + 16 * s2 + 8 * hl);
+          o[db] = mfma16<PE>(av, pb[kb][s2], o[db]);
         }
       }
     }
-    if (j + 1 < nt) swrite((j + 1) & 1);
+  };
+
+  const bool wave_live = qw0 < n;
+  // tile j holds keys the wave can see
+  auto live = [&](int j) { return j < nt && wave_live && !(CAUSAL && j * BK > qw0 + 31); };
+  auto needs_mask = [&](int j) { return (j * BK + BK > n) || (CAUSAL && j * BK + BK - 1 > qw0); };
+
+  // Prologue: K_0, V_0, K_1 into LDS; S_0.
+  load_k(0);
+  load_v(0);
+  store_k(0);
+  store_v(0);
+  if (nt > 1) {
+    load_k(1);
+    store_k(1);
+  }
+  __syncthreads();
+  f32x16_t s[KB];
+  if (live(0)) scores(0, s);
+  __syncthreads();  // K slot 0 is refilled during iteration 0
+
+  for (int j = 0; j < nt; ++j) {
+    const bool more_v = j + 1 < nt, more_k = j + 2 < nt;
+    if (more_v) load_v(j + 1);
+    if (more_k) load_k(j + 2);
+    const bool lj = live(j), ln = live(j + 1);
+    f32x16_t sn[KB];
+    u32x4_t pb[KB][2];
+    if (lj && ln && !needs_mask(j)) {
+      // steady state: scores of tile j+1 overlap the softmax of tile j
+      scores((j + 1) & 1, sn);
+      softmax(s, pb);
+    } else {
+      if (ln) scores((j + 1) & 1, sn);
+      if (lj) {
+        if (needs_mask(j)) mask(s, j * BK);
+        softmax(s, pb);
+      }
+    }
+    if (lj) pv(j & 1, pb);
+    if (more_v) store_v((j + 1) & 1);
+    if (more_k) store_k(j & 1);
     __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = sn[kb];
   }
 
   // Epilogue: O = o / l once per row; LSE = ln 2 * (m2 + log2 l).
-  const float lt = lp + __shfl_xor(lp, 32);
+  const float lt = pair_sum(lp);
   if (qrow < n) {
     const float inv = a.o_mult / lt;
     uint16_t* Og = (uint16_t*)a.o + head_off + (size_t)qrow * D;
@@ -360,6 +450,297 @@ void fwd_mfma16(FwdArgs a) {
         const int d = db * 32 + 8 * g + 4 * hl;
         const uint32_t x0 = pack2<PE>(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
         const uint32_t x1 = pack2<PE>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+        *(u32x2_t*)(Og + d) = u32x2_t{x0, x1};
+      }
+    }
+    if (hl == 0 && a.lse) a.lse[(size_t)tl.bh * n + qrow] = (m2 + __log2f(lt)) * kLn2;
+  }
+}
+// ---------------------------------------------------------------------------
+// Direct-to-LDS kernel for f16 / bf16 inputs. Eight waves (256 query rows)
+// per workgroup, 64-key tiles, and an NS-stage ring of K/V tiles in LDS that
+// the buffer unit fills directly (buffer_load ... lds): no staging registers,
+// no VALU work to move tiles, and NS - 1 tiles of prefetch to hide memory
+// latency. Loads past the end of a head return zeros.
+//
+// LDS layouts. K rows are stored as they are in memory but with their
+// 16-byte chunks XOR-swizzled by row, so that the 16 rows one MFMA operand
+// read touches fall in distinct bank groups. V rows are stored the same way
+// (another swizzle) and read with the transposing LDS read
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// i % 4 of the 8-byte chunks addressed by lanes i / 4, 4 + i / 4, 8 + i / 4
+// and 12 + i / 4. When those four lanes address four consecutive key rows at
+// one group of four d-columns, every lane receives four consecutive keys at
+// its own d-column -- the A operand of O^T = V^T P^T -- without a transpose
+// on the write side.
+//
+// Each ring slot is its own __shared__ array and the key loop is unrolled
+// over the slots, so the compiler can tell the slot being filled from the
+// slot being read and does not wait for the newest loads.
+// ---------------------------------------------------------------------------
+constexpr int kDirectWaves = 8;
+constexpr int kDirectThreads = 64 * kDirectWaves;
+constexpr int kDirectBq = 32 * kDirectWaves;
+#ifndef FA_STAGES
+#define FA_STAGES 4
+#endif
+
+template <int D>
+struct DirectLayout {
+  static constexpr int BK = 64;                 // keys per tile
+  static constexpr int ROWB = D * 2;            // bytes per K or V row
+  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int TILE_B = BK * ROWB;      // bytes per K (or V) tile
+  static constexpr int LPW = TILE_B / 1024 / kDirectWaves;  // 1 KiB loads per wave per tile
+  static_assert(LPW >= 1, "tile too small for the wave count");
+  // chunk swizzles (see the comment above)
+  __device__ static int kswz(int row) { return CPR == 16 ? (row & 15) : ((row >> 1) & 7); }
+  __device__ static int vswz(int row) { return CPR == 16 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+};
+
+template <int BYTES>
+struct LdsSlot {
+  __attribute__((aligned(1024))) uint8_t k[BYTES];
+  __attribute__((aligned(1024))) uint8_t v[BYTES];
+};
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ inline u32x2_t lds_read_tr16(const uint8_t* p) {
+  const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, r);
+}
+
+// One 16-byte buffer load per lane straight into LDS: lane i writes
+// lds + 16 * i. lds must be the same for the whole wave (it goes to M0).
+__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint8_t* lds, uint32_t voffset) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "{m0}"(m0)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <Elt IN, int D, bool CAUSAL>
+__global__ __launch_bounds__(kDirectThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_direct(FwdArgs a) {
+  using L = DirectLayout<D>;
+  constexpr int BK = L::BK, ROWB = L::ROWB, TILE_B = L::TILE_B, LPW = L::LPW;
+  constexpr int NS = FA_STAGES;
+  constexpr int KB = BK / 32;          // 32-key blocks per tile
+  constexpr int NKS = D / 16;          // MFMA k-steps of Q K^T
+  constexpr int NDB = D / 32;          // 32-column blocks of O
+
+  __shared__ LdsSlot<TILE_B> ring0, ring1, ring2, ring3;
+  static_assert(NS >= 2 && NS <= 4, "stages");
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, lr = lane & 31, hl = lane >> 5;
+  const int n = a.n;
+  const int tiles = (n + kDirectBq - 1) / kDirectBq;
+  const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
+  const int q0 = tl.t * kDirectBq;
+  const int qw0 = q0 + 32 * w;
+  const int qrow = qw0 + lr;
+  const size_t head_off = (size_t)tl.bh * (size_t)n * D;
+  const uint32_t head_bytes = (uint32_t)n * ROWB;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint8_t*)a.q + head_off * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint8_t*)a.k + head_off * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint8_t*)a.v + head_off * 2, head_bytes);
+
+  int nt;
+  if (CAUSAL) {
+    const int last = min(q0 + kDirectBq, n) - 1;
+    nt = last / BK + 1;
+  } else {
+    nt = (n + BK - 1) / BK;
+  }
+
+  // Per-lane source offsets of this wave's share of a tile (tile 0).
+  uint32_t koff[LPW], voff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int byte = (w * LPW + i) * 1024 + lane * 16;
+    const int row = byte / ROWB, p = (byte % ROWB) / 16;
+    koff[i] = (uint32_t)(row * ROWB + (p ^ L::kswz(row)) * 16);
+    voff[i] = (uint32_t)(row * ROWB + (p ^ L::vswz(row)) * 16);
+  }
+  // Issue the loads of tile t into a slot; tiles past the loop load nothing
+  // (an offset past the buffer end returns zeros without a memory access),
+  // so every step issues the same number of loads. The copies are issued
+  // through inline assembly: the compiler does not track them, and the
+  // explicit vmcnt wait plus barrier in each step orders them.
+  auto issue = [&](LdsSlot<TILE_B>& slot, int t) __attribute__((always_inline)) {
+    const uint32_t base = t < nt ? (uint32_t)t * TILE_B : 0x80000000u;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      lds_dma16(rk, slot.k + (w * LPW + i) * 1024, base + koff[i]);
+      lds_dma16(rv, slot.v + (w * LPW + i) * 1024, base + voff[i]);
+    }
+  };
+
+  // Q fragments (B operand of S^T = K Q^T), complete before the ring starts.
+  u32x4_t qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    qf[ks] = bload16(rq, ((uint32_t)qrow * D + ks * 16 + hl * 8) * 2);
+  wait_vmcnt<0>();
+
+  // Per-lane LDS read offsets.
+  const int krow = perm32(lr);
+  const int kswz = L::kswz(krow);
+  const int grp = lane >> 4, li = lane & 15;
+  const int vrow0 = 8 * hl + (li >> 2);                 // + kb*32 + 16*s2 + 4*r
+  const int vswz = L::vswz(vrow0);
+  const int vcol = 16 * (grp & 1) + 4 * (li & 3);       // + db*32 (d-column of the 8-byte chunk)
+
+  const float c = a.c;
+  float m2 = -INFINITY, lp = 0.f;
+  f32x16_t o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = f32x16_t{};
+  const bool wave_live = qw0 < n;
+  auto live = [&](int j) __attribute__((always_inline)) { return wave_live && !(CAUSAL && j * BK > qw0 + 31); };
+  auto needs_mask = [&](int j) __attribute__((always_inline)) { return (j * BK + BK > n) || (CAUSAL && j * BK + BK - 1 > qw0); };
+
+  auto compute = [&](const LdsSlot<TILE_B>& slot, int j) __attribute__((always_inline)) {
+    // S^T = K Q^T
+    f32x16_t s[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4_t av = *(const u32x4_t*)(slot.k + (kb * 32 + krow) * ROWB +
+                                             (((2 * ks + hl) ^ kswz) * 16));
+        s[kb] = mfma16<IN>(av, qf[ks], s[kb]);
+      }
+    }
+    if (needs_mask(j)) {
+      const int kbase = j * BK;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kbase + kb * 32 + 16 * (i >> 3) + 8 * hl + (i & 7);
+          const bool ok = key < n && (!CAUSAL || key <= qrow);
+          s[kb][i] = ok ? s[kb][i] : -INFINITY;
+        }
+      }
+    }
+    // online softmax with the lazy rescale
+    float mx = s[0][0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+    for (int kb = 1; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = pair_max(mx);
+    const float mc = mx * c;
+    const bool up = mc > m2 + kLazy;
+    const float m_use = up ? mc : m2;
+    const float alpha = fast_exp2(m2 - m_use);
+    const float nm = -m_use;
+    float ls = 0.f;
+    u32x4_t pb[KB][2];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[kb][i], c, nm));
+        const float p1 = fast_exp2(__builtin_fmaf(s[kb][i + 1], c, nm));
+        ls += p0 + p1;
+        pb[kb][i >> 3][(i & 7) >> 1] = pack2<IN>(p0, p1);
+      }
+    }
+    lp = __builtin_fmaf(alpha, lp, ls);
+    m2 = m_use;
+    if (__any(up)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+    }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int row = kb * 32 + 16 * s2 + vrow0;
+          const int col = db * 32 + vcol;
+          const uint8_t* p0 = slot.v + row * ROWB + (((col >> 3) ^ vswz) * 16) + ((col & 4) << 1);
+          const u32x2_t lo = lds_read_tr16(p0);
+          const u32x2_t hi = lds_read_tr16(p0 + 4 * ROWB);
+          o[db] = mfma16<IN>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pb[kb][s2], o[db]);
+        }
+      }
+    }
+  };
+
+  auto slot_ref = [&](auto S) __attribute__((always_inline)) -> LdsSlot<TILE_B>& {
+    if constexpr (decltype(S)::value == 0) return ring0;
+    else if constexpr (decltype(S)::value == 1) return ring1;
+    else if constexpr (decltype(S)::value == 2) return ring2;
+    else return ring3;
+  };
+  // One step: tile j lives in slot S; the slot of tile j - 1 is refilled
+  // with tile j + NS - 1 once every wave is past tile j - 1.
+  auto step = [&](auto S, int j) __attribute__((always_inline)) {
+    using SN = std::integral_constant<int, (decltype(S)::value + NS - 1) % NS>;
+    wait_vmcnt<(NS - 2) * 2 * LPW>();  // this wave's share of tile j has landed
+    __syncthreads();                   // ... and every other wave's
+    issue(slot_ref(SN{}), j + NS - 1);
+    if (live(j)) compute(slot_ref(S), j);
+  };
+
+  // Zero the ring once, so that rows a load leaves unwritten can never hold
+  // NaN patterns (P is 0 there, but 0 * NaN is NaN).
+  {
+    LdsSlot<TILE_B>* slots[4] = {&ring0, &ring1, &ring2, &ring3};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      u32x4_t* p = (u32x4_t*)slots[s];
+      for (int i = tid; i < (int)(sizeof(LdsSlot<TILE_B>) / 16); i += kDirectThreads)
+        p[i] = u32x4_t{0, 0, 0, 0};
+    }
+  }
+  __syncthreads();
+
+  // prologue: tiles 0 .. NS-2
+  issue(ring0, 0);
+  if constexpr (NS > 2) issue(ring1, 1);
+  if constexpr (NS > 3) issue(ring2, 2);
+
+  for (int j0 = 0; j0 < nt; j0 += NS) {
+    step(std::integral_constant<int, 0>{}, j0);
+    if (j0 + 1 < nt) step(std::integral_constant<int, 1>{}, j0 + 1);
+    if constexpr (NS > 2) if (j0 + 2 < nt) step(std::integral_constant<int, 2>{}, j0 + 2);
+    if constexpr (NS > 3) if (j0 + 3 < nt) step(std::integral_constant<int, 3>{}, j0 + 3);
+  }
+  wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
+
+  // Epilogue: O = o / l once per row; LSE = ln 2 * (m2 + log2 l).
+  const float lt = pair_sum(lp);
+  if (qrow < n) {
+    const float inv = a.o_mult / lt;
+    uint16_t* Og = (uint16_t*)a.o + head_off + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + 8 * g + 4 * hl;
+        const uint32_t x0 = pack2<IN>(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+        const uint32_t x1 = pack2<IN>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
         *(u32x2_t*)(Og + d) = u32x2_t{x0, x1};
       }
     }
@@ -534,10 +915,11 @@ void fwd_mfma32(FwdArgs a) {
 }
 
 template <typename K>
-hipError_t launch(K kernel, const FwdArgs& a, hipStream_t stream) {
-  const int tiles = (a.n + kBq - 1) / kBq;
+hipError_t launch(K kernel, const FwdArgs& a, hipStream_t stream, int rows = kBq,
+                  int threads = kThreads) {
+  const int tiles = (a.n + rows - 1) / rows;
   const unsigned grid = (unsigned)a.bh * (unsigned)tiles;
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -545,8 +927,11 @@ template <Elt E, int D>
 hipError_t dispatch_causal(const FwdArgs& a, hipStream_t s) {
   if constexpr (E == Elt::F32) {
     return a.causal ? launch(fwd_mfma32<D, true>, a, s) : launch(fwd_mfma32<D, false>, a, s);
-  } else {
+  } else if constexpr (E == Elt::FP8) {
     return a.causal ? launch(fwd_mfma16<E, D, true>, a, s) : launch(fwd_mfma16<E, D, false>, a, s);
+  } else {
+    return a.causal ? launch(fwd_direct<E, D, true>, a, s, kDirectBq, kDirectThreads)
+                    : launch(fwd_direct<E, D, false>, a, s, kDirectBq, kDirectThreads);
   }
 }
 
