@@ -33,6 +33,8 @@ METRIC = "attn fwd TFLOP/s & % of bf16 MFMA peak (h32, n8192, d_k128, causal)"
 # published 2.5 PFLOP/s bf16/fp16, 5.0 fp8 and 157.3 fp32 figures).
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "fp8": 5033.2, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
+# the kernel each input type runs on
+KERNEL_OF_DTYPE = {"bf16": "fwd_direct", "f16": "fwd_direct", "fp8": "fwd_mfma16", "f32": "fwd_mfma32"}
 KERNEL_SOURCES = ("transformer_attention_08_amd/csrc/fa_fwd.hip",
                   "transformer_attention_08_amd/csrc/fa_api.cpp",
                   "transformer_attention_08_amd/csrc/fa_kernels.h")
@@ -117,8 +119,8 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3_8b_bf16_causal")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -197,7 +199,7 @@ def main(argv=None):
         "ms_min": round(min(per), 5),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": traffic,
-                     "kernel": "fwd_mfma16" if w.dtype != "f32" else "fwd_mfma32",
+                     "kernel": KERNEL_OF_DTYPE[w.dtype],
                      "min_hbm_bytes": min_hbm_bytes(w)},
     }
     if not args.no_cpu_baseline:

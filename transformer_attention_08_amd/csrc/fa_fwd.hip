@@ -203,7 +203,8 @@ void fwd_mfma16(FwdArgs a) {
   uint8_t* const vls = smem + 2 * K_BYTES;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, lr = lane & 31, hl = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, provably uniform
+  const int lane = tid & 63, lr = lane & 31, hl = lane >> 5;
   const int n = a.n;
   const int tiles = (n + kBq - 1) / kBq;
   const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
@@ -478,7 +479,16 @@ void fwd_mfma16(FwdArgs a) {
 // over the slots, so the compiler can tell the slot being filled from the
 // slot being read and does not wait for the newest loads.
 // ---------------------------------------------------------------------------
-constexpr int kDirectWaves = 8;
+#ifndef FA_PAIR_BARRIER
+#define FA_PAIR_BARRIER 0
+#endif
+#ifndef FA_DIRECT_WAVES
+#define FA_DIRECT_WAVES 8
+#endif
+#ifndef FA_DIRECT_KEYS
+#define FA_DIRECT_KEYS 64
+#endif
+constexpr int kDirectWaves = FA_DIRECT_WAVES;
 constexpr int kDirectThreads = 64 * kDirectWaves;
 constexpr int kDirectBq = 32 * kDirectWaves;
 #ifndef FA_STAGES
@@ -487,7 +497,8 @@ constexpr int kDirectBq = 32 * kDirectWaves;
 
 template <int D>
 struct DirectLayout {
-  static constexpr int BK = 64;                 // keys per tile
+  // keys per tile (64 when a smaller tile would leave a wave without a load)
+  static constexpr int BK = FA_DIRECT_KEYS * D * 2 >= 1024 * kDirectWaves ? FA_DIRECT_KEYS : 64;
   static constexpr int ROWB = D * 2;            // bytes per K or V row
   static constexpr int CPR = D / 8;             // 16-byte chunks per row
   static constexpr int TILE_B = BK * ROWB;      // bytes per K (or V) tile
@@ -543,7 +554,8 @@ void fwd_direct(FwdArgs a) {
   static_assert(NS >= 2 && NS <= 4, "stages");
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, lr = lane & 31, hl = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, provably uniform
+  const int lane = tid & 63, lr = lane & 31, hl = lane >> 5;
   const int n = a.n;
   const int tiles = (n + kDirectBq - 1) / kDirectBq;
   const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
@@ -651,6 +663,8 @@ void fwd_direct(FwdArgs a) {
     const float m_use = up ? mc : m2;
     const float alpha = fast_exp2(m2 - m_use);
     const float nm = -m_use;
+    // l sums the fp32 p: a sum of 16-bit rounded p would carry their 2^-9
+    // relative rounding into l and so into the log-sum-exp
     float ls = 0.f;
     u32x4_t pb[KB][2];
 #pragma unroll
@@ -669,13 +683,13 @@ void fwd_direct(FwdArgs a) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[db] *= alpha;
     }
-    // O^T += V^T P^T
+    // O^T += V^T P^T; consecutive MFMAs go to different accumulators
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
+      for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
+        for (int db = 0; db < NDB; ++db) {
           const int row = kb * 32 + 16 * s2 + vrow0;
           const int col = db * 32 + vcol;
           const uint8_t* p0 = slot.v + row * ROWB + (((col >> 3) ^ vswz) * 16) + ((col & 4) << 1);
@@ -716,6 +730,29 @@ void fwd_direct(FwdArgs a) {
   }
   __syncthreads();
 
+#if FA_PAIR_BARRIER
+  // One barrier per pair of tiles: pair p holds tiles 2p, 2p+1 in slots
+  // (2p % 4, 2p % 4 + 1); at its start the pair's loads are awaited and the
+  // next pair is loaded into the slots of the previous pair.
+  static_assert(NS == 4, "pairs need four slots");
+  issue(ring0, 0);
+  issue(ring1, 1);
+  for (int j0 = 0; j0 < nt; j0 += 4) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    issue(ring2, j0 + 2);
+    issue(ring3, j0 + 3);
+    if (live(j0)) compute(ring0, j0);
+    if (j0 + 1 < nt && live(j0 + 1)) compute(ring1, j0 + 1);
+    if (j0 + 2 >= nt) break;
+    wait_vmcnt<0>();
+    __syncthreads();
+    issue(ring0, j0 + 4);
+    issue(ring1, j0 + 5);
+    if (live(j0 + 2)) compute(ring2, j0 + 2);
+    if (j0 + 3 < nt && live(j0 + 3)) compute(ring3, j0 + 3);
+  }
+#else
   // prologue: tiles 0 .. NS-2
   issue(ring0, 0);
   if constexpr (NS > 2) issue(ring1, 1);
@@ -727,6 +764,7 @@ void fwd_direct(FwdArgs a) {
     if constexpr (NS > 2) if (j0 + 2 < nt) step(std::integral_constant<int, 2>{}, j0 + 2);
     if constexpr (NS > 3) if (j0 + 3 < nt) step(std::integral_constant<int, 3>{}, j0 + 3);
   }
+#endif
   wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
 
   // Epilogue: O = o / l once per row; LSE = ln 2 * (m2 + log2 l).
@@ -770,7 +808,8 @@ void fwd_mfma32(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, lr = lane & 31, hl = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, provably uniform
+  const int lane = tid & 63, lr = lane & 31, hl = lane >> 5;
   const int n = a.n;
   const int tiles = (n + kBq - 1) / kBq;
   const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
