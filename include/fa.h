@@ -53,6 +53,8 @@
 #ifndef FA_MI355X_FA_H
 #define FA_MI355X_FA_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -104,6 +106,43 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                    int batch, int heads, int n, int d_k, float scale, int causal,
                    float q_descale, float k_descale, float v_descale, void* stream);
+
+/*
+ * fa_forward_splitkv -- fa_forward with the keys of every (batch, head) cut
+ * into `splits` contiguous blocks that separate workgroups process, followed
+ * by the log-sum-exp merge of their partial results:
+ *     LSE = ln sum_g e^{LSE_g},   O = sum_g e^{LSE_g - LSE} O_g
+ * where O_g and LSE_g are the output and log-sum-exp of the row over block g
+ * alone. The merge is the associative combine of per-block softmax states
+ * ("Mastering FlashAttention: The Algebraic Foundation", deep-insight
+ * takeaways: log-sum-exp lets blocks recombine without global
+ * synchronisation). It raises the parallelism of problems with few
+ * (batch, head, query tile) units. The result equals fa_forward's up to
+ * rounding.
+ *
+ *   splits      requested number of key blocks, 1 .. 256. Block g holds
+ *               keys [g*B, min(n, (g+1)*B)) with B = 64 * ceil(ceil(n /
+ *               splits) / 64), so ceil(n / B) blocks are used (one block:
+ *               plain fa_forward, no workspace). The workspace holds fp32
+ *               O_g [blocks][batch][heads][n][d_k] from byte 0 and fp32
+ *               LSE_g [blocks][batch][heads][n] from the next multiple of
+ *               256 bytes.
+ *   workspace   caller-owned device memory, 16-byte aligned, at least
+ *               fa_splitkv_workspace_size(...) bytes, not overlapping any
+ *               other argument; its contents on entry are ignored and on
+ *               return are unspecified (fp32 partial outputs and LSEs)
+ * Other arguments as fa_forward. Extra status codes: FA_ERR_UNSUPPORTED for
+ * splits out of range, FA_ERR_NULL / FA_ERR_ALIGN / FA_ERR_ALIAS for the
+ * workspace, FA_ERR_SHAPE when workspace_bytes is too small. Two kernels are
+ * enqueued on `stream` (the blocks, then the merge).
+ */
+int fa_forward_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int batch, int heads, int n, int d_k, float scale, int causal, int dtype,
+                       int splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fa_forward_splitkv needs for these sizes; 0 when the keys
+ * would not be split (or the sizes are invalid). Pure host computation. */
+size_t fa_splitkv_workspace_size(int batch, int heads, int n, int d_k, int splits);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -99,6 +99,56 @@ def test_valid_call_without_gpu_reports_hip_error(lib):
     assert lib.fa_last_hip_error() != 0
 
 
+def block_keys(n, splits):
+    """Keys per split-KV block, the rule stated in include/fa.h."""
+    per = -(-n // splits)
+    return 64 * -(-per // 64)
+
+
+@pytest.mark.parametrize("n,splits", [(1, 1), (100, 1), (100, 2), (64, 2), (65, 2), (8192, 7),
+                                      (8192, 256), (300, 256), (1000, 3)])
+def test_splitkv_workspace_size_follows_the_block_rule(lib, n, splits):
+    b, h, d = 2, 3, 128
+    bk = block_keys(n, splits)
+    used = -(-n // bk)
+    got = lib.fa_splitkv_workspace_size(b, h, n, d, splits)
+    if used == 1:
+        assert got == 0
+    else:
+        o_bytes = used * b * h * n * d * 4
+        lse_off = -(-o_bytes // 256) * 256
+        assert got == lse_off + used * b * h * n * 4
+
+
+def test_splitkv_workspace_size_rejects_bad_sizes(lib):
+    for args in [(0, 1, 10, 64, 2), (1, 1, 0, 64, 2), (1, 1, 10, 96, 2), (1, 1, 1000, 64, 0),
+                 (1, 1, 1000, 64, 257)]:
+        assert lib.fa_splitkv_workspace_size(*args) == 0
+
+
+def test_splitkv_validation(lib):
+    W = BASE + 6 * SPAN
+    def c(splits=4, ws=W, wsb=1 << 30, **kw):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, b=1, h=2, n=1000, d=128, scale=0.125, causal=1, dtype=2)
+        a.update(kw)
+        return lib.fa_forward_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["b"], a["h"], a["n"],
+                                      a["d"], a["scale"], a["causal"], a["dtype"], splits, ws, wsb, None)
+    assert c(n=0) == 2                      # ordinary validation first
+    assert c(splits=0) == 4 and c(splits=257) == 4
+    assert c(ws=None) == 1
+    assert c(ws=W + 8) == 5
+    need = lib.fa_splitkv_workspace_size(1, 2, 1000, 128, 4)
+    assert need > 0 and c(wsb=need - 1) == 2
+    assert c(ws=Q) == 7 and c(ws=O - 64) == 7
+    assert c(ws=L) == 7
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="needs a host without a visible GPU")
+def test_splitkv_valid_call_without_gpu_reports_hip_error(lib):
+    W = BASE + 6 * SPAN
+    assert lib.fa_forward_splitkv(Q, K, V, O, L, 1, 2, 1000, 128, 0.125, 1, 2, 4, W, 1 << 30, None) == 9
+
+
 def test_binding_rejects_bad_tensors():
     x = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError):

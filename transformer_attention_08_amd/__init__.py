@@ -32,8 +32,8 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_DTYPE",
           4: "FA_ERR_UNSUPPORTED", 5: "FA_ERR_ALIGN", 6: "FA_ERR_SCALE", 7: "FA_ERR_ALIAS",
           8: "FA_ERR_OVERFLOW", 9: "FA_ERR_HIP"}
 
-EXPORTS = ("fa_forward", "fa_forward_fp8", "fa_status_string", "fa_last_hip_error",
-           "fa_abi_version")
+EXPORTS = ("fa_forward", "fa_forward_fp8", "fa_forward_splitkv", "fa_splitkv_workspace_size",
+           "fa_status_string", "fa_last_hip_error", "fa_abi_version")
 
 _lib = None
 
@@ -58,6 +58,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_forward.restype = i
     lib.fa_forward_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, f, f, f, vp]
     lib.fa_forward_fp8.restype = i
+    sz = ctypes.c_size_t
+    lib.fa_forward_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, vp, sz, vp]
+    lib.fa_forward_splitkv.restype = i
+    lib.fa_splitkv_workspace_size.argtypes = [i, i, i, i, i]
+    lib.fa_splitkv_workspace_size.restype = sz
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_hip_error.argtypes = []
@@ -145,3 +150,32 @@ def forward_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_descale: fl
                             float(v_descale), _stream(q.device))
     _check(st)
     return out, lse
+
+
+def splitkv_workspace_size(batch: int, heads: int, n: int, d_k: int, splits: int) -> int:
+    """Bytes of workspace ``forward_splitkv`` needs (0: the keys are not split)."""
+    return int(load_library().fa_splitkv_workspace_size(batch, heads, n, d_k, splits))
+
+
+def forward_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, splits: int,
+                    causal: bool = False, scale: Optional[float] = None,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None):
+    """``fa_forward_splitkv``: keys cut into ``splits`` blocks, partial results
+    merged by their log-sum-exp. Returns (O, LSE, workspace); the workspace
+    (uint8 device tensor, allocated here unless given) holds the per-block
+    partials after the call."""
+    lib = load_library()
+    out, lse = _prepare(q, k, v, out, lse)
+    b, h, n, d = q.shape
+    need = splitkv_workspace_size(b, h, n, d, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib.fa_forward_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, h, n, d, s,
+                                1 if causal else 0, _DTYPE_CODE[q.dtype], int(splits),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(q.device))
+    _check(st)
+    return out, lse, workspace
+

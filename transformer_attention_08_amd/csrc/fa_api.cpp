@@ -1,6 +1,7 @@
 // Host front end of the C ABI declared in include/fa.h: argument validation
 // (pure host code, before any HIP call), then one kernel launch.
 #include <cmath>
+#include <cstddef>
 #include <cstdint>
 #include <cfloat>
 
@@ -60,8 +61,33 @@ int validate(const void* q, const void* k, const void* v, void* o, const float* 
   return FA_OK;
 }
 
+// Keys per split-KV block for a requested number of blocks (a multiple of
+// 64, the coarsest key tile of the kernels), and the number of blocks that
+// results.
+constexpr int kMaxSplits = 256;
+int split_keys_for(int n, int splits) {
+  const int64_t per = ((int64_t)n + splits - 1) / splits;
+  return (int)(((per + 63) / 64) * 64);
+}
+int splits_used(int n, int splits) {
+  const int sk = split_keys_for(n, splits);
+  return (n + sk - 1) / sk;
+}
+struct SplitLayout {
+  size_t o_bytes, lse_off, total;
+};
+SplitLayout split_layout(int batch, int heads, int n, int d_k, int used) {
+  const size_t rows = (size_t)batch * heads * n * (size_t)used;
+  SplitLayout s;
+  s.o_bytes = rows * d_k * 4;
+  s.lse_off = (s.o_bytes + 255) / 256 * 256;
+  s.total = s.lse_off + rows * 4;
+  return s;
+}
+
 int run(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int heads,
-        int n, int d_k, float qk_scale, int causal, int dtype, float o_mult, void* stream) {
+        int n, int d_k, float qk_scale, int causal, int dtype, float o_mult, void* stream,
+        int splits = 1, void* workspace = nullptr) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) {
@@ -83,7 +109,31 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int ba
     a.c = c;
     a.o_mult = o_mult;
     a.elt = static_cast<fa::Elt>(dtype);
+    a.split_keys = n;
+    a.splits = 1;
+    a.part_o = nullptr;
+    a.part_lse = nullptr;
+    const int used = splits > 1 ? splits_used(n, splits) : 1;
+    if (used > 1) {
+      const SplitLayout sl = split_layout(batch, heads, n, d_k, used);
+      a.split_keys = split_keys_for(n, splits);
+      a.splits = used;
+      a.part_o = (float*)workspace;
+      a.part_lse = (float*)((char*)workspace + sl.lse_off);
+    }
     e = fa::launch_forward(a, static_cast<hipStream_t>(stream));
+    if (e == hipSuccess && used > 1) {
+      fa::CombineArgs cb;
+      cb.part_o = a.part_o;
+      cb.part_lse = a.part_lse;
+      cb.o = o;
+      cb.lse = lse;
+      cb.rows = batch * heads * n;
+      cb.d = d_k;
+      cb.splits = used;
+      cb.out = dtype == FA_F32 ? fa::Elt::F32 : dtype == FA_F16 ? fa::Elt::F16 : fa::Elt::BF16;
+      e = fa::launch_combine(cb, static_cast<hipStream_t>(stream));
+    }
   }
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
@@ -113,6 +163,43 @@ int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* 
   const float qk = (float)((double)scale * q_descale * k_descale);
   if (!std::isfinite((float)(qk * kLog2e))) return FA_ERR_SCALE;
   return run(q, k, v, o, lse, batch, heads, n, d_k, qk, causal, FA_FP8_E4M3, v_descale, stream);
+}
+
+size_t fa_splitkv_workspace_size(int batch, int heads, int n, int d_k, int splits) {
+  if (batch < 1 || heads < 1 || n < 1 || (d_k != 64 && d_k != 128) || splits < 1 ||
+      splits > kMaxSplits)
+    return 0;
+  const int used = splits_used(n, splits);
+  if (used <= 1) return 0;
+  return split_layout(batch, heads, n, d_k, used).total;
+}
+
+int fa_forward_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                       int heads, int n, int d_k, float scale, int causal, int dtype, int splits,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = validate(q, k, v, o, lse, batch, heads, n, d_k, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (splits < 1 || splits > kMaxSplits) return FA_ERR_UNSUPPORTED;
+  const int used = splits_used(n, splits);
+  if (used > 1) {
+    if (!workspace) return FA_ERR_NULL;
+    if ((uintptr_t)workspace % 16) return FA_ERR_ALIGN;
+    const size_t need = split_layout(batch, heads, n, d_k, used).total;
+    if (workspace_bytes < need) return FA_ERR_SHAPE;
+    const int64_t rows = (int64_t)batch * heads * n;
+    const int in_bytes = dtype == FA_F32 ? 4 : dtype == FA_FP8_E4M3 ? 1 : 2;
+    const int out_bytes = dtype == FA_F32 ? 4 : 2;
+    const Range rw{(uintptr_t)workspace, (uintptr_t)workspace + need};
+    const Range rq{(uintptr_t)q, (uintptr_t)q + (uintptr_t)(rows * d_k * in_bytes)};
+    const Range rk{(uintptr_t)k, (uintptr_t)k + (uintptr_t)(rows * d_k * in_bytes)};
+    const Range rv{(uintptr_t)v, (uintptr_t)v + (uintptr_t)(rows * d_k * in_bytes)};
+    const Range ro{(uintptr_t)o, (uintptr_t)o + (uintptr_t)(rows * d_k * out_bytes)};
+    if (overlap(rw, rq) || overlap(rw, rk) || overlap(rw, rv) || overlap(rw, ro)) return FA_ERR_ALIAS;
+    if (lse && overlap(rw, Range{(uintptr_t)lse, (uintptr_t)lse + (uintptr_t)(rows * 4)}))
+      return FA_ERR_ALIAS;
+  }
+  return run(q, k, v, o, lse, batch, heads, n, d_k, scale, causal, dtype, 1.0f, stream, splits,
+             workspace);
 }
 
 const char* fa_status_string(int status) {

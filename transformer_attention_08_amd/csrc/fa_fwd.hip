@@ -85,6 +85,49 @@ __device__ inline int perm32(int m) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Key tiles [lo, hi) of this workgroup: its block of keys (grid dimension y),
+// cut at the last query row of the tile under a causal mask.
+struct KeyTiles {
+  int lo, hi;
+};
+template <int BK>
+__device__ inline KeyTiles key_tiles(const FwdArgs& a, int q_end, bool causal) {
+  const int kbeg = blockIdx.y * a.split_keys;
+  int kend = min(a.n, kbeg + a.split_keys);
+  if (causal) kend = min(kend, q_end);
+  const int lo = kbeg / BK;
+  return {lo, kend > kbeg ? (kend + BK - 1) / BK : lo};
+}
+
+// The reference max used for the exponentials: a row that has seen no
+// visible key yet (possible in a later key block) keeps -inf as its max but
+// exponentiates against 0, so its weights are exactly 0 rather than NaN.
+__device__ inline float exp_ref(float m) { return m == -INFINITY ? 0.f : m; }
+
+// Split-KV partial result of one row (lane halves hold d-columns as in the
+// O^T accumulator): O_g = o / l (times o_mult), LSE_g; zeros and -inf when
+// the block held no visible key.
+template <int NDB>
+__device__ inline void store_partial(const FwdArgs& a, int bh, int qrow, int hl, const f32x16_t (&o)[NDB],
+                                     float m2, float lt) {
+  constexpr int D = NDB * 32;
+  const size_t row = ((size_t)blockIdx.y * a.bh + bh) * a.n + qrow;
+  float* po = a.part_o + row * D;
+  const float inv = lt > 0.f ? a.o_mult / lt : 0.f;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = db * 32 + 8 * g + 4 * hl;
+      u32x4_t x;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = __float_as_uint(o[db][4 * g + r] * inv);
+      *(u32x4_t*)(po + d) = x;
+    }
+  }
+  if (hl == 0) a.part_lse[row] = lt > 0.f ? (m2 + __log2f(lt)) * kLn2 : -INFINITY;
+}
+
 template <Elt E>
 __device__ inline uint32_t pack2(float a, float b) {
   if constexpr (E == Elt::F16) {
@@ -233,13 +276,8 @@ void fwd_mfma16(FwdArgs a) {
     }
   }
 
-  int nt;
-  if (CAUSAL) {
-    const int last = min(q0 + kBq, n) - 1;
-    nt = last / BK + 1;
-  } else {
-    nt = (n + BK - 1) / BK;
-  }
+  const KeyTiles kt = key_tiles<BK>(a, min(q0 + kBq, n), CAUSAL);
+  const int j_lo = kt.lo, nt = kt.hi;  // key tiles j_lo .. nt-1
 
   // ---- staging of global tiles through registers
   u32x4_t kst[NLD], vst[NLD];
@@ -346,8 +384,8 @@ void fwd_mfma16(FwdArgs a) {
     const float mc = mx * c;
     const bool up = mc > m2 + kLazy;
     const float m_use = up ? mc : m2;
-    const float alpha = fast_exp2(m2 - m_use);
-    const float nm = -m_use;
+    const float alpha = fast_exp2(m2 - exp_ref(m_use));
+    const float nm = -exp_ref(m_use);
     float ls = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -399,21 +437,23 @@ void fwd_mfma16(FwdArgs a) {
   auto live = [&](int j) { return j < nt && wave_live && !(CAUSAL && j * BK > qw0 + 31); };
   auto needs_mask = [&](int j) { return (j * BK + BK > n) || (CAUSAL && j * BK + BK - 1 > qw0); };
 
-  // Prologue: K_0, V_0, K_1 into LDS; S_0.
-  load_k(0);
-  load_v(0);
+  // Prologue: K, V of tile j_lo and K of tile j_lo + 1 into LDS; S of j_lo.
+  // Slots are indexed relative to j_lo.
+  load_k(j_lo);
+  load_v(j_lo);
   store_k(0);
   store_v(0);
-  if (nt > 1) {
-    load_k(1);
+  if (nt > j_lo + 1) {
+    load_k(j_lo + 1);
     store_k(1);
   }
   __syncthreads();
   f32x16_t s[KB];
-  if (live(0)) scores(0, s);
-  __syncthreads();  // K slot 0 is refilled during iteration 0
+  if (live(j_lo)) scores(0, s);
+  __syncthreads();  // K slot 0 is refilled during the first iteration
 
-  for (int j = 0; j < nt; ++j) {
+  for (int j = j_lo; j < nt; ++j) {
+    const int r = j - j_lo;
     const bool more_v = j + 1 < nt, more_k = j + 2 < nt;
     if (more_v) load_v(j + 1);
     if (more_k) load_k(j + 2);
@@ -422,18 +462,18 @@ void fwd_mfma16(FwdArgs a) {
     u32x4_t pb[KB][2];
     if (lj && ln && !needs_mask(j)) {
       // steady state: scores of tile j+1 overlap the softmax of tile j
-      scores((j + 1) & 1, sn);
+      scores((r + 1) & 1, sn);
       softmax(s, pb);
     } else {
-      if (ln) scores((j + 1) & 1, sn);
+      if (ln) scores((r + 1) & 1, sn);
       if (lj) {
         if (needs_mask(j)) mask(s, j * BK);
         softmax(s, pb);
       }
     }
-    if (lj) pv(j & 1, pb);
-    if (more_v) store_v((j + 1) & 1);
-    if (more_k) store_k(j & 1);
+    if (lj) pv(r & 1, pb);
+    if (more_v) store_v((r + 1) & 1);
+    if (more_k) store_k(r & 1);
     __syncthreads();
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) s[kb] = sn[kb];
@@ -441,7 +481,9 @@ void fwd_mfma16(FwdArgs a) {
 
   // Epilogue: O = o / l once per row; LSE = ln 2 * (m2 + log2 l).
   const float lt = pair_sum(lp);
-  if (qrow < n) {
+  if (qrow < n && a.part_o) {
+    store_partial<NDB>(a, tl.bh, qrow, hl, o, m2, lt);
+  } else if (qrow < n) {
     const float inv = a.o_mult / lt;
     uint16_t* Og = (uint16_t*)a.o + head_off + (size_t)qrow * D;
 #pragma unroll
@@ -479,9 +521,6 @@ void fwd_mfma16(FwdArgs a) {
 // over the slots, so the compiler can tell the slot being filled from the
 // slot being read and does not wait for the newest loads.
 // ---------------------------------------------------------------------------
-#ifndef FA_PAIR_BARRIER
-#define FA_PAIR_BARRIER 0
-#endif
 #ifndef FA_DIRECT_WAVES
 #define FA_DIRECT_WAVES 8
 #endif
@@ -568,13 +607,8 @@ void fwd_direct(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint8_t*)a.k + head_off * 2, head_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint8_t*)a.v + head_off * 2, head_bytes);
 
-  int nt;
-  if (CAUSAL) {
-    const int last = min(q0 + kDirectBq, n) - 1;
-    nt = last / BK + 1;
-  } else {
-    nt = (n + BK - 1) / BK;
-  }
+  const KeyTiles kt = key_tiles<BK>(a, min(q0 + kDirectBq, n), CAUSAL);
+  const int j_lo = kt.lo, nt = kt.hi;  // key tiles j_lo .. nt-1 (ring slots relative to j_lo)
 
   // Per-lane source offsets of this wave's share of a tile (tile 0).
   uint32_t koff[LPW], voff[LPW];
@@ -661,8 +695,8 @@ void fwd_direct(FwdArgs a) {
     const float mc = mx * c;
     const bool up = mc > m2 + kLazy;
     const float m_use = up ? mc : m2;
-    const float alpha = fast_exp2(m2 - m_use);
-    const float nm = -m_use;
+    const float alpha = fast_exp2(m2 - exp_ref(m_use));
+    const float nm = -exp_ref(m_use);
     // l sums the fp32 p: a sum of 16-bit rounded p would carry their 2^-9
     // relative rounding into l and so into the log-sum-exp
     float ls = 0.f;
@@ -730,46 +764,24 @@ void fwd_direct(FwdArgs a) {
   }
   __syncthreads();
 
-#if FA_PAIR_BARRIER
-  // One barrier per pair of tiles: pair p holds tiles 2p, 2p+1 in slots
-  // (2p % 4, 2p % 4 + 1); at its start the pair's loads are awaited and the
-  // next pair is loaded into the slots of the previous pair.
-  static_assert(NS == 4, "pairs need four slots");
-  issue(ring0, 0);
-  issue(ring1, 1);
-  for (int j0 = 0; j0 < nt; j0 += 4) {
-    wait_vmcnt<0>();
-    __syncthreads();
-    issue(ring2, j0 + 2);
-    issue(ring3, j0 + 3);
-    if (live(j0)) compute(ring0, j0);
-    if (j0 + 1 < nt && live(j0 + 1)) compute(ring1, j0 + 1);
-    if (j0 + 2 >= nt) break;
-    wait_vmcnt<0>();
-    __syncthreads();
-    issue(ring0, j0 + 4);
-    issue(ring1, j0 + 5);
-    if (live(j0 + 2)) compute(ring2, j0 + 2);
-    if (j0 + 3 < nt && live(j0 + 3)) compute(ring3, j0 + 3);
-  }
-#else
-  // prologue: tiles 0 .. NS-2
-  issue(ring0, 0);
-  if constexpr (NS > 2) issue(ring1, 1);
-  if constexpr (NS > 3) issue(ring2, 2);
+  // prologue: tiles j_lo .. j_lo + NS - 2
+  issue(ring0, j_lo);
+  if constexpr (NS > 2) issue(ring1, j_lo + 1);
+  if constexpr (NS > 3) issue(ring2, j_lo + 2);
 
-  for (int j0 = 0; j0 < nt; j0 += NS) {
+  for (int j0 = j_lo; j0 < nt; j0 += NS) {
     step(std::integral_constant<int, 0>{}, j0);
     if (j0 + 1 < nt) step(std::integral_constant<int, 1>{}, j0 + 1);
     if constexpr (NS > 2) if (j0 + 2 < nt) step(std::integral_constant<int, 2>{}, j0 + 2);
     if constexpr (NS > 3) if (j0 + 3 < nt) step(std::integral_constant<int, 3>{}, j0 + 3);
   }
-#endif
   wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
 
   // Epilogue: O = o / l once per row; LSE = ln 2 * (m2 + log2 l).
   const float lt = pair_sum(lp);
-  if (qrow < n) {
+  if (qrow < n && a.part_o) {
+    store_partial<NDB>(a, tl.bh, qrow, hl, o, m2, lt);
+  } else if (qrow < n) {
     const float inv = a.o_mult / lt;
     uint16_t* Og = (uint16_t*)a.o + head_off + (size_t)qrow * D;
 #pragma unroll
@@ -833,13 +845,8 @@ void fwd_mfma32(FwdArgs a) {
     }
   }
 
-  int nt;
-  if (CAUSAL) {
-    const int last = min(q0 + kBq, n) - 1;
-    nt = last / BK + 1;
-  } else {
-    nt = (n + BK - 1) / BK;
-  }
+  const KeyTiles kt = key_tiles<BK>(a, min(q0 + kBq, n), CAUSAL);
+  const int j_lo = kt.lo, nt = kt.hi;  // key tiles j_lo .. nt-1
 
   u32x4_t kreg[NLD], vreg[NLD];
   auto gload = [&](int j) {
@@ -872,16 +879,17 @@ void fwd_mfma32(FwdArgs a) {
   const float c = a.c;
   const bool wave_live = qw0 < n;
 
-  gload(0);
+  gload(j_lo);
   swrite(0);
   __syncthreads();
 
-  for (int j = 0; j < nt; ++j) {
+  for (int j = j_lo; j < nt; ++j) {
+    const int r = j - j_lo;  // double-buffer slots are relative to j_lo
     if (j + 1 < nt) gload(j + 1);
     const int kbase = j * BK;
     const bool skip = !wave_live || (CAUSAL && kbase > qw0 + 31);
     if (!skip) {
-      const float* kl = smem + (j & 1) * STAGE;
+      const float* kl = smem + (r & 1) * STAGE;
       const float* vl = kl + K_FL;
       f32x16_t s = f32x16_t{};
       const float* kr = kl + lr * KS + hl * HALF;
@@ -907,8 +915,8 @@ void fwd_mfma32(FwdArgs a) {
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m2, mx * c);
-      const float alpha = fast_exp2(m2 - m_new);
-      const float nm = -m_new;
+      const float alpha = fast_exp2(m2 - exp_ref(m_new));
+      const float nm = -exp_ref(m_new);
       float ls = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -930,12 +938,14 @@ void fwd_mfma32(FwdArgs a) {
         }
       }
     }
-    if (j + 1 < nt) swrite((j + 1) & 1);
+    if (j + 1 < nt) swrite((r + 1) & 1);
     __syncthreads();
   }
 
   const float lt = lp + __shfl_xor(lp, 32);
-  if (qrow < n) {
+  if (qrow < n && a.part_o) {
+    store_partial<NDB>(a, tl.bh, qrow, hl, o, m2, lt);
+  } else if (qrow < n) {
     const float inv = a.o_mult / lt;
     float* Og = (float*)a.o + head_off + (size_t)qrow * D;
 #pragma unroll
@@ -958,7 +968,59 @@ hipError_t launch(K kernel, const FwdArgs& a, hipStream_t stream, int rows = kBq
                   int threads = kThreads) {
   const int tiles = (a.n + rows - 1) / rows;
   const unsigned grid = (unsigned)a.bh * (unsigned)tiles;
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, stream, a);
+  hipLaunchKernelGGL(kernel, dim3(grid, (unsigned)a.splits), dim3(threads), 0, stream, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV combine: for each row, LSE = ln sum_g e^{LSE_g} and
+// O = sum_g e^{LSE_g - LSE} O_g (the associative merge of per-block softmax
+// states, "Mastering FlashAttention: The Algebraic Foundation"). One wave per
+// row; each lane owns d-columns lane and lane + 64. Memory-bound.
+// ---------------------------------------------------------------------------
+template <Elt OUT, int D>
+__global__ __launch_bounds__(256) void combine_splits(CombineArgs a) {
+  constexpr float kLog2e = 1.44269504088896340736f;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= a.rows) return;
+  const size_t plane = (size_t)a.rows;  // rows per split
+  float mx = -INFINITY;
+  for (int g = 0; g < a.splits; ++g) mx = fmaxf(mx, a.part_lse[g * plane + row]);
+  // every row has a visible key in some block, so mx is finite
+  float wsum = 0.f, acc0 = 0.f, acc1 = 0.f;
+  for (int g = 0; g < a.splits; ++g) {
+    const float lg = a.part_lse[g * plane + row];
+    const float wg = lg == -INFINITY ? 0.f : fast_exp2((lg - mx) * kLog2e);
+    const float* po = a.part_o + (g * plane + row) * D;
+    wsum += wg;
+    acc0 = __builtin_fmaf(wg, po[lane], acc0);
+    if constexpr (D == 128) acc1 = __builtin_fmaf(wg, po[lane + 64], acc1);
+  }
+  const float inv = 1.f / wsum;
+  if constexpr (OUT == Elt::F32) {
+    float* o = (float*)a.o + (size_t)row * D;
+    o[lane] = acc0 * inv;
+    if constexpr (D == 128) o[lane + 64] = acc1 * inv;
+  } else if constexpr (OUT == Elt::F16) {
+    _Float16* o = (_Float16*)a.o + (size_t)row * D;
+    o[lane] = (_Float16)(acc0 * inv);
+    if constexpr (D == 128) o[lane + 64] = (_Float16)(acc1 * inv);
+  } else {
+    __bf16* o = (__bf16*)a.o + (size_t)row * D;
+    o[lane] = (__bf16)(acc0 * inv);
+    if constexpr (D == 128) o[lane + 64] = (__bf16)(acc1 * inv);
+  }
+  if (lane == 0 && a.lse) a.lse[row] = mx + __logf(wsum);
+}
+
+template <Elt OUT>
+hipError_t launch_combine_t(const CombineArgs& a, hipStream_t s) {
+  const unsigned grid = (unsigned)((a.rows + 3) / 4);
+  if (a.d == 64)
+    hipLaunchKernelGGL((combine_splits<OUT, 64>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((combine_splits<OUT, 128>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -980,6 +1042,14 @@ hipError_t dispatch_d(const FwdArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+  switch (a.out) {
+    case Elt::F32: return launch_combine_t<Elt::F32>(a, stream);
+    case Elt::F16: return launch_combine_t<Elt::F16>(a, stream);
+    default: return launch_combine_t<Elt::BF16>(a, stream);
+  }
+}
 
 hipError_t launch_forward(const FwdArgs& a, hipStream_t stream) {
   switch (a.elt) {

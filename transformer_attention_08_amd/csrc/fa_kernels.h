@@ -22,10 +22,32 @@ struct FwdArgs {
   float c;         // scale (times both fp8 descales) times log2(e)
   float o_mult;    // multiplier applied to O in the epilogue (v descale; 1 otherwise)
   Elt elt;
+  // Split-KV: the keys are cut into blocks of split_keys (a multiple of 64;
+  // n when the keys are not split) and grid dimension y runs over the blocks.
+  // When part_o is set, each block writes its partial result there instead of
+  // o / lse: O_g normalised by its own row sum, fp32 [splits][bh][n][d], and
+  // LSE_g, fp32 [splits][bh][n] (-inf where the block holds no visible key).
+  int split_keys;
+  int splits;
+  float* part_o;
+  float* part_lse;
+};
+
+// Merge of split-KV partials into O and LSE (the log-sum-exp combine).
+struct CombineArgs {
+  const float* part_o;
+  const float* part_lse;
+  void* o;
+  float* lse;      // may be null
+  int rows;        // batch * heads * n
+  int d;
+  int splits;
+  Elt out;         // F32, F16 or BF16
 };
 
 // Enqueue the forward kernel for validated arguments. Returns the HIP status
 // of the launch.
 hipError_t launch_forward(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
 }  // namespace fa
