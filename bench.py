@@ -11,7 +11,7 @@ HBM traffic measured by rocprofv3 counters when the stored measurement
 belongs to the current kernel source) and the CPU oracle timed on a bounded
 sample of the same workload on this host's cores.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--splits S] [--no-cpu-baseline]
     python bench.py --copy-calibration      # plain copy of known size (counter scale)
 """
 from __future__ import annotations
@@ -35,8 +35,9 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "fp8": 5033.2, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 # the kernel each input type runs on
 KERNEL_OF_DTYPE = {"bf16": "fwd_direct", "f16": "fwd_direct", "fp8": "fwd_mfma16", "f32": "fwd_mfma32"}
+# the files the forward kernels and their launch shape are compiled from; a
+# stored traffic measurement is valid only for the sources it was taken on
 KERNEL_SOURCES = ("transformer_attention_08_amd/csrc/fa_fwd.hip",
-                  "transformer_attention_08_amd/csrc/fa_api.cpp",
                   "transformer_attention_08_amd/csrc/fa_kernels.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama3_8b_bf16_causal.json")
 
@@ -123,6 +124,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3_8b_bf16_causal")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--splits", type=int, default=1,
+                    help="cut the keys into this many blocks (fa_forward_splitkv) and merge")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args(argv)
@@ -150,9 +153,19 @@ def main(argv=None):
     d = inp.to(dev)
     o = torch.empty(w.batch, w.heads, w.n, w.d_k, dtype=workload.torch_dtype(w.out_dtype), device=dev)
     lse = torch.empty(w.batch, w.heads, w.n, dtype=torch.float32, device=dev)
+    if args.splits > 1 and w.dtype == "fp8" and (inp.q_descale, inp.k_descale, inp.v_descale) != (1, 1, 1):
+        print("the split-KV entry takes e4m3 with unit descales only", file=sys.stderr)
+        return 2
+    ws = None
+    if args.splits > 1:
+        need = fa.splitkv_workspace_size(w.batch, w.heads, w.n, w.d_k, args.splits)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
 
     def step():
-        if w.dtype == "fp8":
+        if ws is not None:
+            fa.forward_splitkv(d.q, d.k, d.v, args.splits, causal=w.causal, scale=w.scale, out=o,
+                               lse=lse, workspace=ws)
+        elif w.dtype == "fp8":
             fa.forward_fp8(d.q, d.k, d.v, inp.q_descale, inp.k_descale, inp.v_descale,
                            causal=w.causal, scale=w.scale, out=o, lse=lse)
         else:
@@ -179,8 +192,12 @@ def main(argv=None):
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     traffic = stored_traffic(w.name)
+    split_tag = f", split-KV {args.splits}" if ws is not None else ""
+    if ws is not None:
+        traffic = None  # the stored counters cover the unsplit kernel only
     line = {
-        "metric": METRIC if w.name == "llama3_8b_bf16_causal" else f"attn fwd TFLOP/s ({w.name})",
+        "metric": (METRIC if w.name == "llama3_8b_bf16_causal" and ws is None
+                   else f"attn fwd TFLOP/s ({w.name}{split_tag})"),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -193,13 +210,13 @@ def main(argv=None):
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "n": w.n, "d_k": w.d_k,
-                   "causal": w.causal, "flops_per_step": flops},
+                   "causal": w.causal, "flops_per_step": flops, "splits": args.splits},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "ms_median": round(statistics.median(per), 5),
         "ms_min": round(min(per), 5),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": traffic,
-                     "kernel": KERNEL_OF_DTYPE[w.dtype],
+                     "kernel": KERNEL_OF_DTYPE[w.dtype] + ("+combine_splits" if ws is not None else ""),
                      "min_hbm_bytes": min_hbm_bytes(w)},
     }
     if not args.no_cpu_baseline:

@@ -975,52 +975,63 @@ hipError_t launch(K kernel, const FwdArgs& a, hipStream_t stream, int rows = kBq
 // ---------------------------------------------------------------------------
 // Split-KV combine: for each row, LSE = ln sum_g e^{LSE_g} and
 // O = sum_g e^{LSE_g - LSE} O_g (the associative merge of per-block softmax
-// states, "Mastering FlashAttention: The Algebraic Foundation"). One wave per
-// row; each lane owns d-columns lane and lane + 64. Memory-bound.
+// states, "Mastering FlashAttention: The Algebraic Foundation"). Memory-bound:
+// each lane owns 4 consecutive d-columns of one row (16-byte loads), so a
+// wave covers 64 / (D / 4) rows and a 256-thread workgroup kCombineRows(D).
 // ---------------------------------------------------------------------------
+template <int D>
+constexpr int kCombineRows = 256 / (D / 4);
+
 template <Elt OUT, int D>
 __global__ __launch_bounds__(256) void combine_splits(CombineArgs a) {
   constexpr float kLog2e = 1.44269504088896340736f;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  constexpr int kLanesPerRow = D / 4;
+  const int row = blockIdx.x * kCombineRows<D> + (int)threadIdx.x / kLanesPerRow;
+  const int col = ((int)threadIdx.x % kLanesPerRow) * 4;
   if (row >= a.rows) return;
   const size_t plane = (size_t)a.rows;  // rows per split
   float mx = -INFINITY;
   for (int g = 0; g < a.splits; ++g) mx = fmaxf(mx, a.part_lse[g * plane + row]);
   // every row has a visible key in some block, so mx is finite
-  float wsum = 0.f, acc0 = 0.f, acc1 = 0.f;
+  float wsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
   for (int g = 0; g < a.splits; ++g) {
     const float lg = a.part_lse[g * plane + row];
     const float wg = lg == -INFINITY ? 0.f : fast_exp2((lg - mx) * kLog2e);
-    const float* po = a.part_o + (g * plane + row) * D;
+    const float4 po = *(const float4*)(a.part_o + (g * plane + row) * D + col);
     wsum += wg;
-    acc0 = __builtin_fmaf(wg, po[lane], acc0);
-    if constexpr (D == 128) acc1 = __builtin_fmaf(wg, po[lane + 64], acc1);
+    acc.x = __builtin_fmaf(wg, po.x, acc.x);
+    acc.y = __builtin_fmaf(wg, po.y, acc.y);
+    acc.z = __builtin_fmaf(wg, po.z, acc.z);
+    acc.w = __builtin_fmaf(wg, po.w, acc.w);
   }
   const float inv = 1.f / wsum;
+  const size_t at = (size_t)row * D + col;
   if constexpr (OUT == Elt::F32) {
-    float* o = (float*)a.o + (size_t)row * D;
-    o[lane] = acc0 * inv;
-    if constexpr (D == 128) o[lane + 64] = acc1 * inv;
-  } else if constexpr (OUT == Elt::F16) {
-    _Float16* o = (_Float16*)a.o + (size_t)row * D;
-    o[lane] = (_Float16)(acc0 * inv);
-    if constexpr (D == 128) o[lane + 64] = (_Float16)(acc1 * inv);
+    *(float4*)((float*)a.o + at) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   } else {
-    __bf16* o = (__bf16*)a.o + (size_t)row * D;
-    o[lane] = (__bf16)(acc0 * inv);
-    if constexpr (D == 128) o[lane + 64] = (__bf16)(acc1 * inv);
+    using T = typename std::conditional<OUT == Elt::F16, _Float16, __bf16>::type;
+    struct alignas(8) T4 { T v[4]; };
+    T4 r;
+    r.v[0] = (T)(acc.x * inv);
+    r.v[1] = (T)(acc.y * inv);
+    r.v[2] = (T)(acc.z * inv);
+    r.v[3] = (T)(acc.w * inv);
+    *(T4*)((T*)a.o + at) = r;
   }
-  if (lane == 0 && a.lse) a.lse[row] = mx + __logf(wsum);
+  if (col == 0 && a.lse) a.lse[row] = mx + __logf(wsum);
 }
 
 template <Elt OUT>
 hipError_t launch_combine_t(const CombineArgs& a, hipStream_t s) {
-  const unsigned grid = (unsigned)((a.rows + 3) / 4);
-  if (a.d == 64)
+  if (a.d == 64) {
+    const unsigned grid = (unsigned)((a.rows + kCombineRows<64> - 1) / kCombineRows<64>);
     hipLaunchKernelGGL((combine_splits<OUT, 64>), dim3(grid), dim3(256), 0, s, a);
-  else
+  } else {
+    const unsigned grid = (unsigned)((a.rows + kCombineRows<128> - 1) / kCombineRows<128>);
     hipLaunchKernelGGL((combine_splits<OUT, 128>), dim3(grid), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

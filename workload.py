@@ -71,6 +71,9 @@ WORKLOADS = {
     "llama3_8b_bf16_causal": Workload("llama3_8b_bf16_causal", 1, 32, 8192, 128, "bf16", True),
     "long_ctx_bf16_causal": Workload("long_ctx_bf16_causal", 1, 32, 32768, 128, "bf16", True),
     "fp8_e4m3_nomask": Workload("fp8_e4m3_nomask", 1, 32, 8192, 128, "fp8", False, qk_mult=4.0),
+    # grids far below the chip's 256 CUs: the cases the split-KV path is for
+    "two_heads_bf16": Workload("two_heads_bf16", 1, 2, 4096, 128, "bf16", False),
+    "four_heads_long_bf16_causal": Workload("four_heads_long_bf16_causal", 1, 4, 16384, 128, "bf16", True),
 }
 
 
