@@ -1,4 +1,4 @@
-"""CPU oracle for the exact scaled-dot-product attention forward pass.
+"""CPU oracle for exact scaled-dot-product attention, forward and gradients.
 
 TEST INFRASTRUCTURE ONLY. This package is the plain, slow, obviously correct
 reference that the HIP kernels are checked against. Only the test suite, the
@@ -13,9 +13,12 @@ Contents
                 probabilities P per full row), a literal streaming version of
                 the online-softmax recurrence, the associative merge of
                 (m, l, o) states, and a 50-digit ``decimal`` brute force.
+  backward   -- the gradients dQ, dK, dV of the definition (S, P, dP, dS
+                materialised), plus row and key-column samplers for full sizes.
   accounting -- FLOP, byte and exponential counts of the method.
 
-Parity status: every function here is pinned by ``tests/test_oracle.py``
+Parity status: every function here is pinned by ``tests/test_oracle.py`` and
+``tests/test_oracle_backward.py``
 against brute force, closed forms and invariants the pages fix. The numeric
 tolerances that the GPU must meet are not derivable from the pages (they
 announce an error analysis but never print it); those numbers are stated,
@@ -30,5 +33,11 @@ from .reference import (  # noqa: F401
     online_attention,
     tile_state,
     finalize_state,
+)
+from .backward import (  # noqa: F401
+    attention_backward,
+    backward_rows,
+    backward_key_columns,
+    head_statistics,
 )
 from .accounting import flops, min_hbm_bytes, exp_count, score_matrix_ratio  # noqa: F401
