@@ -117,6 +117,84 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}))
 
 
+def backward_flops(w) -> float:
+    """The five products of the gradient (S recomputed, dP, dV, dQ, dK), 2*n*n*d_k
+    FLOP each per head; halved under a causal mask (2.5 x the forward count)."""
+    f = 10.0 * w.batch * w.heads * w.n * w.n * w.d_k
+    return f / 2 if w.causal else f
+
+
+def time_steps(step, stream, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"# warmup done ({warmup} calls)", file=sys.stderr, flush=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return evs[0].elapsed_time(evs[-1]) / steps, per
+
+
+def bench_backward(args, w):
+    """One step = one fa_backward call (both passes) on the workload, with the
+    forward's O and LSE computed once beforehand."""
+    import torch
+
+    import transformer_attention_08_amd as fa
+    import workload
+
+    if w.dtype not in ("bf16", "f16"):
+        print("the backward runs on f16 / bf16 workloads", file=sys.stderr)
+        return 2
+    inp, do = workload.make_inputs_with_grad(w.batch, w.heads, w.n, w.d_k, w.dtype, args.seed)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = inp.to(dev)
+    dog = do.to(dev)
+    o, lse = fa.forward(d.q, d.k, d.v, causal=w.causal, scale=w.scale)
+    dq, dk, dv = (torch.empty_like(d.q) for _ in range(3))
+    ws = torch.empty(fa.backward_workspace_size(w.batch, w.heads, w.n), dtype=torch.uint8, device=dev)
+
+    def step():
+        fa.backward(d.q, d.k, d.v, o, lse, dog, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv,
+                    workspace=ws)
+
+    ms, per = time_steps(step, torch.cuda.current_stream(dev), args.steps, args.warmup)
+    flops = backward_flops(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    line = {
+        "metric": f"attn bwd TFLOP/s ({w.name})",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) Q, K, V, dO of the workload's shape)",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "n": w.n, "d_k": w.d_k,
+                   "causal": w.causal, "flops_per_step": flops, "pass": "backward"},
+        "pct_of_peak": round(100.0 * tflops / peak, 2),
+        "ms_median": round(statistics.median(per), 5),
+        "ms_min": round(min(per), 5),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": None,
+                     "kernel": "bwd_dq+bwd_dkdv"},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +204,8 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--splits", type=int, default=1,
                     help="cut the keys into this many blocks (fa_forward_splitkv) and merge")
+    ap.add_argument("--backward", action="store_true",
+                    help="time fa_backward (dQ, dK, dV) instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args(argv)
@@ -147,6 +227,8 @@ def main(argv=None):
 
     w = workload.WORKLOADS[args.workload]
     fa.load_library()
+    if args.backward:
+        return bench_backward(args, w)
     inp = workload.workload_inputs(w, args.seed)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

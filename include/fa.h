@@ -35,10 +35,12 @@
  * log2(e) into it and evaluates exponentials as exp2).
  *
  * Ownership. The caller owns every buffer. The library allocates no device
- * or host memory per call, keeps no workspace and no n x n buffer, and holds
- * no state beyond per-process kernel registration. q, k, v are only read.
- * o and lse are written in full (every element of the valid rows) and must
- * not overlap q, k, v or each other. Calls are reentrant and thread-safe.
+ * or host memory per call and no n x n buffer; the entry points that need
+ * scratch memory (fa_forward_splitkv, fa_backward) take it from the caller
+ * as a workspace argument. It holds no state beyond per-process kernel
+ * registration. Inputs are only read. Outputs are written in full (every
+ * element of the valid rows) and must not overlap the inputs or each other.
+ * Calls are reentrant and thread-safe.
  *
  * Errors. Every entry point returns an fa_status. Arguments are validated on
  * the host before any HIP call; on a validation error nothing is launched
@@ -68,14 +70,16 @@ typedef enum {
 
 typedef enum {
   FA_OK = 0,
-  FA_ERR_NULL = 1,        /* q, k, v or o is NULL                                   */
-  FA_ERR_SHAPE = 2,       /* batch, heads or n < 1                                  */
+  FA_ERR_NULL = 1,        /* a required pointer is NULL                             */
+  FA_ERR_SHAPE = 2,       /* batch, heads or n < 1, or a workspace too small         */
   FA_ERR_DTYPE = 3,       /* dtype is not one of fa_dtype                           */
-  FA_ERR_UNSUPPORTED = 4, /* d_k not in {64, 128}, or causal not in {0, 1}          */
+  FA_ERR_UNSUPPORTED = 4, /* d_k not in {64, 128}, causal not in {0, 1}, or a mode  */
+                          /* this entry point does not offer                       */
   FA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                       */
   FA_ERR_SCALE = 6,       /* scale (or a descale) is not finite, or is negative     */
-  FA_ERR_ALIAS = 7,       /* o or lse overlaps q, k, v, or each other               */
+  FA_ERR_ALIAS = 7,       /* an output or workspace overlaps an input or an output  */
   FA_ERR_OVERFLOW = 8,    /* the problem exceeds the kernel's index or grid range   */
+                          /* (one head's bytes must stay below 2^31)               */
   FA_ERR_HIP = 9          /* the HIP runtime refused a call; see fa_last_hip_error  */
 } fa_status;
 
@@ -143,6 +147,43 @@ int fa_forward_splitkv(const void* q, const void* k, const void* v, void* o, flo
 /* Workspace bytes fa_forward_splitkv needs for these sizes; 0 when the keys
  * would not be split (or the sizes are invalid). Pure host computation. */
 size_t fa_splitkv_workspace_size(int batch, int heads, int n, int d_k, int splits);
+
+/*
+ * fa_backward -- gradients of the attention of fa_forward (f16 / bf16).
+ *
+ * Given dO = dL/dO of a scalar loss L, with P = softmax_rows(scale Q K^T +
+ * mask) as in fa_forward:
+ *     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),   D = rowsum(dO * O),
+ *     dQ = scale dS K,   dK = scale dS^T Q
+ * (the chain rule through the equation of the slide "Attention is where
+ * tokens meet"). P is never stored: it is recomputed on-chip from Q, K and
+ * the forward's LSE, in two passes (article "Mastering FlashAttention: The
+ * Algebraic Foundation", technical deep dive): a query-major pass writes dQ,
+ * a key-major pass writes dK and dV. The result is deterministic (no atomics).
+ *
+ *   q, k, v     the forward's inputs, [batch, heads, n, d_k] (read only)
+ *   o, lse      the forward's outputs O [batch, heads, n, d_k] and fp32 LSE
+ *               [batch, heads, n] for the same q, k, v, scale and causal flag
+ *               (read only)
+ *   dout        dO, [batch, heads, n, d_k] (read only)
+ *   dq, dk, dv  outputs, [batch, heads, n, d_k], same type as q
+ *   dtype       FA_F16 or FA_BF16 (others: FA_ERR_UNSUPPORTED)
+ *   workspace   caller-owned device memory, 16-byte aligned, at least
+ *               fa_backward_workspace_size(batch, heads, n) bytes; on return
+ *               it holds fp32 D [batch, heads, n] from byte 0 and
+ *               -LSE * log2(e) from the next multiple of 256 bytes
+ * Other arguments as fa_forward. All pointers are required (FA_ERR_NULL) and
+ * 16-byte aligned. dq, dk, dv and the workspace must not overlap any input or
+ * each other (FA_ERR_ALIAS); workspace_bytes too small gives FA_ERR_SHAPE.
+ * Two kernels are enqueued on `stream`.
+ */
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, int batch, int heads, int n,
+                int d_k, float scale, int causal, int dtype, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fa_backward needs (0 for invalid sizes). Pure host code. */
+size_t fa_backward_workspace_size(int batch, int heads, int n);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -155,3 +155,55 @@ def test_binding_rejects_bad_tensors():
         fa.forward(x, x, x)  # host tensors
     with pytest.raises(ValueError):
         fa.forward(x[0], x[0], x[0])  # wrong rank
+
+
+def test_head_bytes_beyond_32_bit_buffer_range_overflow(lib):
+    # one head of 2^22 rows x 128 bf16 = 1 GiB is fine; f32 doubles it past 2^31
+    assert call(lib, n=(1 << 23) + 64, dtype=2) == 8
+    assert call(lib, n=1 << 22, dtype=0) == 8
+
+
+# ---------------------------------------------------------------- backward
+
+OB, DO, DQ, DK, DV, WS = (BASE + (8 + i) * SPAN for i in range(6))
+
+
+def bcall(lib, q=Q, k=K, v=V, o=OB, do=DO, lse=L, dq=DQ, dk=DK, dv=DV, b=1, h=2, n=100, d=128,
+          scale=0.125, causal=1, dtype=2, ws=WS, wsb=1 << 20):
+    return lib.fa_backward(q, k, v, o, do, lse, dq, dk, dv, b, h, n, d, scale, causal, dtype, ws, wsb,
+                           None)
+
+
+def test_backward_workspace_size(lib):
+    for b, h, n in ((1, 1, 1), (2, 3, 100), (1, 32, 8192)):
+        rows = b * h * n
+        assert lib.fa_backward_workspace_size(b, h, n) == -(-rows * 4 // 256) * 256 + rows * 4
+    assert lib.fa_backward_workspace_size(0, 1, 10) == 0
+    assert lib.fa_backward_workspace_size(1, 1, 0) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(do=None), 1), (dict(lse=None), 1), (dict(dq=None), 1),
+    (dict(dk=None), 1), (dict(dv=None), 1), (dict(ws=None), 1),
+    (dict(n=0), 2), (dict(h=0), 2), (dict(wsb=100 * 2 * 4), 2),
+    (dict(dtype=5), 3), (dict(dtype=0), 4), (dict(dtype=3), 4), (dict(d=96), 4), (dict(causal=2), 4),
+    (dict(dq=DQ + 8), 5), (dict(lse=L + 4), 5), (dict(ws=WS + 8), 5), (dict(do=DO + 2), 5),
+    (dict(scale=float("nan")), 6), (dict(scale=-1.0), 6),
+    (dict(dq=Q), 7), (dict(dk=OB + 64), 7), (dict(dv=DO), 7), (dict(ws=L), 7), (dict(dk=DQ), 7),
+    (dict(ws=DV + 16), 7), (dict(dq=L - 64), 7),
+    (dict(b=65536, h=65536), 8), (dict(n=(1 << 23) + 64), 8),
+])
+def test_backward_validation_errors(lib, kw, status):
+    assert bcall(lib, **kw) == status
+
+
+def test_backward_inputs_may_alias_each_other(lib):
+    # read-only inputs may share memory; with a bad shape the shape error still wins
+    assert bcall(lib, k=Q, v=Q, n=0) == 2
+    if torch.cuda.device_count() == 0:
+        assert bcall(lib, k=Q, v=Q, o=Q, do=Q) == 9
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="needs a host without a visible GPU")
+def test_backward_valid_call_without_gpu_reports_hip_error(lib):
+    assert bcall(lib) == 9

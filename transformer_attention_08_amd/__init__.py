@@ -7,6 +7,7 @@ importing works but every call raises.
 
     o, lse = forward(q, k, v, causal=True)              # f32 / f16 / bf16
     o, lse = forward_fp8(q8, k8, v8, qd, kd, vd)         # e4m3fn + descales
+    dq, dk, dv = backward(q, k, v, o, lse, do, causal=True)   # f16 / bf16
 """
 from __future__ import annotations
 
@@ -33,7 +34,8 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_DTYPE",
           8: "FA_ERR_OVERFLOW", 9: "FA_ERR_HIP"}
 
 EXPORTS = ("fa_forward", "fa_forward_fp8", "fa_forward_splitkv", "fa_splitkv_workspace_size",
-           "fa_status_string", "fa_last_hip_error", "fa_abi_version")
+           "fa_backward", "fa_backward_workspace_size", "fa_status_string", "fa_last_hip_error",
+           "fa_abi_version")
 
 _lib = None
 
@@ -63,6 +65,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_forward_splitkv.restype = i
     lib.fa_splitkv_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_splitkv_workspace_size.restype = sz
+    lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.fa_backward.restype = i
+    lib.fa_backward_workspace_size.argtypes = [i, i, i]
+    lib.fa_backward_workspace_size.restype = sz
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_hip_error.argtypes = []
@@ -179,3 +185,43 @@ def forward_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, splits: i
     _check(st)
     return out, lse, workspace
 
+
+
+def backward_workspace_size(batch: int, heads: int, n: int) -> int:
+    """Bytes of workspace ``backward`` needs."""
+    return int(load_library().fa_backward_workspace_size(batch, heads, n))
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+             dout: torch.Tensor, causal: bool = False, scale: Optional[float] = None,
+             dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+             dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """``fa_backward``: (dQ, dK, dV) of the attention ``forward`` computed, given
+    its O and LSE and the output gradient dO. f16 or bf16, contiguous
+    [batch, heads, n, d_k] device tensors; LSE fp32 [batch, heads, n]."""
+    lib = load_library()
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("backward takes float16 or bfloat16 tensors")
+    for t in (k, v, o, dout):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o and dout must share one shape and dtype")
+    for t in (q, k, v, o, dout, lse):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous device tensors")
+    if q.dim() != 4:
+        raise ValueError("tensors are [batch, heads, n, d_k]")
+    b, h, n, d = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (b, h, n):
+        raise ValueError("lse must be float32 [batch, heads, n]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(backward_workspace_size(b, h, n), dtype=torch.uint8, device=q.device)
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                         _ptr(dk), _ptr(dv), b, h, n, d, s, 1 if causal else 0, _DTYPE_CODE[q.dtype],
+                         _ptr(workspace), workspace.numel() * workspace.element_size(),
+                         _stream(q.device))
+    _check(st)
+    return dq, dk, dv

@@ -1,6 +1,6 @@
 """Build the HIP library ``libfa.so`` in place (gfx950 only).
 
-The library holds the fused attention forward kernels and the C ABI of
+The library holds the fused attention forward and backward kernels and the C ABI of
 ``include/fa.h``. It is compiled with hipcc for ``--offload-arch=gfx950``;
 hipcc cross-compiles without a GPU present.
 """
@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ("fa_fwd.hip", "fa_api.cpp")
+SOURCES = ("fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp")
 ARCH = "gfx950"
 
 

@@ -1,5 +1,6 @@
 // Host front end of the C ABI declared in include/fa.h: argument validation
-// (pure host code, before any HIP call), then one kernel launch.
+// (pure host code, before any HIP call), then the kernel launches.
+#include <algorithm>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -45,8 +46,10 @@ int validate(const void* q, const void* k, const void* v, void* o, const float* 
   if (bh > kMaxGrid || bh * tiles > kMaxGrid) return FA_ERR_OVERFLOW;
   const int in_bytes = dtype == FA_F32 ? 4 : dtype == FA_FP8_E4M3 ? 1 : 2;
   const int out_bytes = dtype == FA_F32 ? 4 : 2;
-  // byte sizes must fit comfortably in 63 bits
+  // byte sizes must fit comfortably in 63 bits, and one head's bytes in the
+  // kernels' 32-bit buffer ranges
   if (rows > (INT64_C(1) << 62) / ((int64_t)d_k * 4)) return FA_ERR_OVERFLOW;
+  if ((int64_t)n * d_k * std::max(in_bytes, out_bytes) > INT32_MAX) return FA_ERR_OVERFLOW;
   const int64_t in_sz = rows * d_k * in_bytes, out_sz = rows * d_k * out_bytes, lse_sz = rows * 4;
 
   const Range rq{(uintptr_t)q, (uintptr_t)q + (uintptr_t)in_sz};
@@ -83,6 +86,60 @@ SplitLayout split_layout(int batch, int heads, int n, int d_k, int used) {
   s.lse_off = (s.o_bytes + 255) / 256 * 256;
   s.total = s.lse_off + rows * 4;
   return s;
+}
+
+// Backward workspace: D = rowsum(dO * O) at byte 0, -LSE*log2(e) from the
+// next multiple of 256 bytes; fp32 [batch][heads][n] each.
+struct BwdLayout {
+  size_t nl_off, total;
+};
+BwdLayout bwd_layout(int batch, int heads, int n) {
+  const size_t rows = (size_t)batch * heads * n;
+  BwdLayout l;
+  l.nl_off = (rows * 4 + 255) / 256 * 256;
+  l.total = l.nl_off + rows * 4;
+  return l;
+}
+
+int validate_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int batch, int heads, int n,
+                 int d_k, float scale, int causal, int dtype, void* workspace,
+                 size_t workspace_bytes) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+  if (batch < 1 || heads < 1 || n < 1) return FA_ERR_SHAPE;
+  if (dtype < FA_F32 || dtype > FA_FP8_E4M3) return FA_ERR_DTYPE;
+  if ((dtype != FA_F16 && dtype != FA_BF16) || (d_k != 64 && d_k != 128) ||
+      (causal != 0 && causal != 1))
+    return FA_ERR_UNSUPPORTED;
+  const uintptr_t ptrs[10] = {(uintptr_t)q,  (uintptr_t)k,  (uintptr_t)v,  (uintptr_t)o,
+                              (uintptr_t)dout, (uintptr_t)lse, (uintptr_t)dq, (uintptr_t)dk,
+                              (uintptr_t)dv, (uintptr_t)workspace};
+  for (uintptr_t p : ptrs)
+    if (p % 16) return FA_ERR_ALIGN;
+  if (!std::isfinite(scale) || scale < 0.f || !std::isfinite((float)(scale * kLog2e)))
+    return FA_ERR_SCALE;
+  const int64_t bh = (int64_t)batch * heads;
+  const int64_t rows = bh * n;
+  if (bh > kMaxGrid || bh * (((int64_t)n + 127) / 128) > kMaxGrid) return FA_ERR_OVERFLOW;
+  if (rows > (INT64_C(1) << 62) / ((int64_t)d_k * 4)) return FA_ERR_OVERFLOW;
+  if ((int64_t)n * d_k * 2 > INT32_MAX) return FA_ERR_OVERFLOW;
+  const BwdLayout wl = bwd_layout(batch, heads, n);
+  if (workspace_bytes < wl.total) return FA_ERR_SHAPE;
+  const uintptr_t t_sz = (uintptr_t)(rows * d_k * 2);
+  const Range ins[6] = {{(uintptr_t)q, (uintptr_t)q + t_sz},       {(uintptr_t)k, (uintptr_t)k + t_sz},
+                        {(uintptr_t)v, (uintptr_t)v + t_sz},       {(uintptr_t)o, (uintptr_t)o + t_sz},
+                        {(uintptr_t)dout, (uintptr_t)dout + t_sz}, {(uintptr_t)lse, (uintptr_t)lse + (uintptr_t)(rows * 4)}};
+  const Range outs[4] = {{(uintptr_t)dq, (uintptr_t)dq + t_sz},
+                         {(uintptr_t)dk, (uintptr_t)dk + t_sz},
+                         {(uintptr_t)dv, (uintptr_t)dv + t_sz},
+                         {(uintptr_t)workspace, (uintptr_t)workspace + wl.total}};
+  for (int i = 0; i < 4; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return FA_ERR_ALIAS;
+  }
+  return FA_OK;
 }
 
 int run(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int heads,
@@ -202,16 +259,62 @@ int fa_forward_splitkv(const void* q, const void* k, const void* v, void* o, flo
              workspace);
 }
 
+size_t fa_backward_workspace_size(int batch, int heads, int n) {
+  if (batch < 1 || heads < 1 || n < 1) return 0;
+  return bwd_layout(batch, heads, n).total;
+}
+
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, int batch, int heads, int n,
+                int d_k, float scale, int causal, int dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  const int st = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, batch, heads, n, d_k, scale,
+                              causal, dtype, workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) {
+    const BwdLayout wl = bwd_layout(batch, heads, n);
+    fa::BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.lse = lse;
+    a.delta = (float*)workspace;
+    a.nlse2 = (float*)((char*)workspace + wl.nl_off);
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.bh = batch * heads;
+    a.n = n;
+    a.d = d_k;
+    a.causal = causal != 0;
+    float c = (float)(scale * kLog2e);
+    if (!(c > 0.f)) c = FLT_MIN;  // as in the forward: a zero scale gives uniform weights
+    a.c = c;
+    a.scale = scale;
+    a.elt = static_cast<fa::Elt>(dtype);
+    e = fa::launch_backward(a, static_cast<hipStream_t>(stream));
+  }
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
-    case FA_ERR_NULL: return "null q, k, v or o pointer";
-    case FA_ERR_SHAPE: return "batch, heads and n must be >= 1";
+    case FA_ERR_NULL: return "null pointer argument";
+    case FA_ERR_SHAPE: return "batch, heads and n must be >= 1 (or workspace too small)";
     case FA_ERR_DTYPE: return "unknown dtype";
-    case FA_ERR_UNSUPPORTED: return "unsupported d_k (64 or 128) or causal flag (0 or 1)";
+    case FA_ERR_UNSUPPORTED: return "unsupported d_k (64 or 128), causal flag (0 or 1), split count or backward dtype";
     case FA_ERR_ALIGN: return "pointer not 16-byte aligned";
     case FA_ERR_SCALE: return "scale or descale not finite, or negative";
-    case FA_ERR_ALIAS: return "o or lse overlaps an input or each other";
+    case FA_ERR_ALIAS: return "an output or workspace overlaps an input or another output";
     case FA_ERR_OVERFLOW: return "problem exceeds the kernel's index or grid range";
     case FA_ERR_HIP: return "HIP runtime error (see fa_last_hip_error)";
     default: return "unknown status";

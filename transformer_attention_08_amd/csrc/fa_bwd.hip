@@ -1,0 +1,515 @@
+// Attention backward pass for gfx950 (CDNA4, MI355X), f16 / bf16.
+//
+// Gradients of O = softmax(S) V with S = scale Q K^T + mask, given dO:
+//   P  = exp(S - LSE)             (recomputed from Q, K and the forward's
+//                                  per-row log-sum-exp; never stored)
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D = rowsum(dO * O)
+//   dQ = scale dS K,  dK = scale dS^T Q.
+// The backward recomputes the attention matrix on-chip in two passes instead
+// of storing it (article "Mastering FlashAttention: The Algebraic
+// Foundation", technical deep dive). Here the two passes are:
+//   1. bwd_dq, query-major: one workgroup per (batch*head, 256 query rows)
+//      streams the K/V tiles like the forward and accumulates dQ in
+//      registers. It also computes D for its rows (from dO and O) and
+//      -LSE*log2(e), and leaves both in the caller's workspace.
+//   2. bwd_dkdv, key-major: one workgroup per (batch*head, 128 keys) streams
+//      the Q / dO tiles (with D and LSE) and accumulates dK and dV.
+// Each pass owns its outputs, so no atomics and no second reduction: the
+// result is deterministic. The price is that S and dP are computed in both
+// passes (7 matrix products instead of the 5 the gradient needs).
+//
+// Register layouts follow the forward kernel: the 32x32 MFMA puts the index
+// a wave owns (queries in pass 1, keys in pass 2) on the lanes, so the
+// per-row or per-key statistics are lane-local; the contraction index of the
+// second product in each pass is permuted (perm32) so that accumulator
+// registers, packed to 16 bits, are directly the B operand of that product.
+//
+// LDS. Tiles are copied straight into LDS by the buffer unit (buffer_load
+// ... lds) through an NS-stage ring. Each tile is read both row-wise (16-byte
+// operand reads, 16 rows per 16 lanes) and transposed (ds_read_b64_tr_b16,
+// 4 consecutive rows x 4 chunks per 32 lanes), so its 16-byte chunks are
+// XOR-swizzled with a function of the row that keeps both access patterns
+// on distinct banks (swz2).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+namespace {
+
+constexpr int kBwdStages = 4;
+
+// Chunk swizzle for rows of D 16-bit elements: bijective on the 16 rows of
+// one row-wise read, and distinct in its upper bits (D = 128: bits 2-3 over
+// the 16 chunks of a 256-byte row; D = 64: bit 2 within a row parity) for
+// the 4 consecutive rows of one transposing read.
+template <int D>
+__device__ inline int swz2(int row) {
+  if constexpr (D == 128)
+    return 4 * (row & 3) + ((row >> 2) & 3);
+  else
+    return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+}
+
+// Sum of the products of 8 16-bit values (fp32). The words are copied out of
+// the vectors before the bit cast: a bit cast applied to a vector element
+// expression read element 0 whatever the index.
+template <Elt E>
+__device__ inline float dot8(u32x4_t a, u32x4_t b) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t ai = a[i], bi = b[i];
+    if constexpr (E == Elt::F16) {
+      const f16x2_t x = __builtin_bit_cast(f16x2_t, ai);
+      const f16x2_t y = __builtin_bit_cast(f16x2_t, bi);
+      s = __builtin_fmaf((float)x[0], (float)y[0], s);
+      s = __builtin_fmaf((float)x[1], (float)y[1], s);
+    } else {
+      s = __builtin_fmaf(__uint_as_float(ai << 16), __uint_as_float(bi << 16), s);
+      s = __builtin_fmaf(__uint_as_float(ai & 0xffff0000u), __uint_as_float(bi & 0xffff0000u), s);
+    }
+  }
+  return s;
+}
+
+// 32 columns (one per lane, rows 4 per register group) of a d-major
+// accumulator -> 8-byte stores of 4 consecutive d values: acc[db][4g + r] is
+// d-column db*32 + 8g + 4*hl + r of this lane's row.
+template <Elt E, int NDB>
+__device__ inline void store_rows(uint16_t* row_ptr, int hl, const f32x16_t (&acc)[NDB], float mult) {
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = db * 32 + 8 * g + 4 * hl;
+      const uint32_t x0 = pack2<E>(acc[db][4 * g] * mult, acc[db][4 * g + 1] * mult);
+      const uint32_t x1 = pack2<E>(acc[db][4 * g + 2] * mult, acc[db][4 * g + 3] * mult);
+      *(u32x2_t*)(row_ptr + d) = u32x2_t{x0, x1};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: dQ. Eight waves, 32 query rows each; 64-key tiles of K and V.
+// Per tile and 32-key block: S^T = K Q^T and dP^T = V dO^T (row-wise reads
+// of K and V), P = exp2(c S - LSE log2 e), dS = P (dP - D), then
+// dQ^T += K^T dS^T with K^T from transposing reads of the same K tile.
+// ---------------------------------------------------------------------------
+constexpr int kDqWaves = 8;
+constexpr int kDqThreads = 64 * kDqWaves;
+constexpr int kDqBq = 32 * kDqWaves;
+
+template <int BYTES>
+struct PairSlot {
+  __attribute__((aligned(1024))) uint8_t a[BYTES];
+  __attribute__((aligned(1024))) uint8_t b[BYTES];
+};
+
+template <Elt IN, int D, bool CAUSAL>
+__global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq(BwdArgs a) {
+  constexpr int ROWB = D * 2, BK = 64, TILE_B = BK * ROWB;
+  constexpr int LPW = TILE_B / 1024 / kDqWaves;  // 1 KiB loads per wave per tile (K and V each)
+  constexpr int NS = kBwdStages;
+  constexpr int KB = BK / 32, NKS = D / 16, NDB = D / 32;
+  static_assert(LPW >= 1, "tile too small for the wave count");
+
+  __shared__ PairSlot<TILE_B> ring0, ring1, ring2, ring3;  // a: K, b: V
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 31, hl = lane >> 5;
+  const int n = a.n;
+  const int tiles = (n + kDqBq - 1) / kDqBq;
+  const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
+  const int q0 = tl.t * kDqBq;
+  const int qw0 = q0 + 32 * w;
+  const int qrow = qw0 + lr;
+  const size_t head_off = (size_t)tl.bh * (size_t)n * D;
+  const uint32_t head_bytes = (uint32_t)n * ROWB;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint8_t*)a.q + head_off * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint8_t*)a.k + head_off * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint8_t*)a.v + head_off * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc((const uint8_t*)a.o + head_off * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc((const uint8_t*)a.dout + head_off * 2, head_bytes);
+
+  const int nt = ((CAUSAL ? min(q0 + kDqBq, n) : n) + BK - 1) / BK;  // key tiles 0 .. nt-1
+
+  uint32_t off[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int byte = (w * LPW + i) * 1024 + lane * 16;
+    const int row = byte / ROWB, p = (byte % ROWB) / 16;
+    off[i] = (uint32_t)(row * ROWB + (p ^ swz2<D>(row)) * 16);
+  }
+  auto issue = [&](PairSlot<TILE_B>& slot, int t) __attribute__((always_inline)) {
+    const uint32_t base = t < nt ? (uint32_t)t * TILE_B : 0x80000000u;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      lds_dma16(rk, slot.a + (w * LPW + i) * 1024, base + off[i]);
+      lds_dma16(rv, slot.b + (w * LPW + i) * 1024, base + off[i]);
+    }
+  };
+
+  // Q and dO fragments (B operands), O only for D = rowsum(dO * O).
+  u32x4_t qf[NKS], gf[NKS];
+  float dpart = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const uint32_t o_ = ((uint32_t)qrow * D + ks * 16 + hl * 8) * 2;
+    qf[ks] = bload16(rq, o_);
+    gf[ks] = bload16(rg, o_);
+    dpart += dot8<IN>(gf[ks], bload16(ro, o_));
+  }
+  const float dsum = pair_sum(dpart);
+  const size_t srow = (size_t)tl.bh * n + qrow;
+  const float nl2 = qrow < n ? -a.lse[srow] * kLog2e : 0.f;
+  if (hl == 0 && qrow < n) {
+    a.delta[srow] = dsum;
+    a.nlse2[srow] = nl2;
+  }
+  wait_vmcnt<0>();
+
+  const int krow = perm32(lr);
+  const int sw_k = swz2<D>(krow);
+  const int grp = lane >> 4, li = lane & 15;
+  const int trow = 8 * hl + (li >> 2);  // + kb*32 + 16*s2 (+4 for the second read)
+  const int sw_lo = swz2<D>(trow), sw_hi = swz2<D>(trow + 4);
+  const int tcol = 16 * (grp & 1) + 4 * (li & 3);  // + db*32
+
+  const float c = a.c;
+  f32x16_t dq[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dq[db] = f32x16_t{};
+  const bool wave_live = qw0 < n;
+  auto live = [&](int j) __attribute__((always_inline)) { return wave_live && !(CAUSAL && j * BK > qw0 + 31); };
+  auto needs_mask = [&](int j) __attribute__((always_inline)) {
+    return (j * BK + BK > n) || (CAUSAL && j * BK + BK - 1 > qw0);
+  };
+
+  auto compute = [&](const PairSlot<TILE_B>& slot, int j) __attribute__((always_inline)) {
+    const bool mask = needs_mask(j);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+      const int row = kb * 32 + krow;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int at = row * ROWB + (((2 * ks + hl) ^ sw_k) * 16);
+        s = mfma16<IN>(*(const u32x4_t*)(slot.a + at), qf[ks], s);
+        dp = mfma16<IN>(*(const u32x4_t*)(slot.b + at), gf[ks], dp);
+      }
+      if (mask) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = j * BK + kb * 32 + 16 * (i >> 3) + 8 * hl + (i & 7);
+          const bool ok = key < n && (!CAUSAL || key <= qrow);
+          s[i] = ok ? s[i] : -INFINITY;
+        }
+      }
+      u32x4_t dsb[2];
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[i], c, nl2));
+        const float p1 = fast_exp2(__builtin_fmaf(s[i + 1], c, nl2));
+        dsb[i >> 3][(i & 7) >> 1] = pack2<IN>(p0 * (dp[i] - dsum), p1 * (dp[i + 1] - dsum));
+      }
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int r = kb * 32 + 16 * s2 + trow;
+          const int col = db * 32 + tcol;
+          const int half = (col & 4) << 1;
+          const u32x2_t lo = lds_read_tr16(slot.a + r * ROWB + (((col >> 3) ^ sw_lo) * 16) + half);
+          const u32x2_t hi = lds_read_tr16(slot.a + (r + 4) * ROWB + (((col >> 3) ^ sw_hi) * 16) + half);
+          dq[db] = mfma16<IN>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, dsb[s2], dq[db]);
+        }
+      }
+    }
+  };
+
+  auto slot_ref = [&](auto S) __attribute__((always_inline)) -> PairSlot<TILE_B>& {
+    if constexpr (decltype(S)::value == 0) return ring0;
+    else if constexpr (decltype(S)::value == 1) return ring1;
+    else if constexpr (decltype(S)::value == 2) return ring2;
+    else return ring3;
+  };
+  auto step = [&](auto S, int j) __attribute__((always_inline)) {
+    using SN = std::integral_constant<int, (decltype(S)::value + NS - 1) % NS>;
+    wait_vmcnt<(NS - 2) * 2 * LPW>();
+    __syncthreads();
+    issue(slot_ref(SN{}), j + NS - 1);
+    if (live(j)) compute(slot_ref(S), j);
+  };
+
+  {
+    PairSlot<TILE_B>* slots[4] = {&ring0, &ring1, &ring2, &ring3};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      u32x4_t* p = (u32x4_t*)slots[s];
+      for (int i = tid; i < (int)(sizeof(PairSlot<TILE_B>) / 16); i += kDqThreads) p[i] = u32x4_t{0, 0, 0, 0};
+    }
+  }
+  __syncthreads();
+
+  issue(ring0, 0);
+  issue(ring1, 1);
+  issue(ring2, 2);
+  for (int j0 = 0; j0 < nt; j0 += NS) {
+    step(std::integral_constant<int, 0>{}, j0);
+    if (j0 + 1 < nt) step(std::integral_constant<int, 1>{}, j0 + 1);
+    if (j0 + 2 < nt) step(std::integral_constant<int, 2>{}, j0 + 2);
+    if (j0 + 3 < nt) step(std::integral_constant<int, 3>{}, j0 + 3);
+  }
+  wait_vmcnt<0>();
+
+  if (qrow < n) store_rows<IN, NDB>((uint16_t*)a.dq + head_off + (size_t)qrow * D, hl, dq, a.scale);
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: dK and dV. Four waves (one per SIMD, so each has the full register
+// file), 32 keys each; 64-query tiles of Q and dO plus their D and
+// -LSE*log2(e). Per tile and 32-query block: S = Q K^T and dP = dO V^T
+// (row-wise reads of Q and dO; K and V of the wave's keys are B operands held
+// in registers), P and dS as in pass 1, then dV^T += dO^T P and
+// dK^T += Q^T dS with dO^T and Q^T from transposing reads.
+// ---------------------------------------------------------------------------
+constexpr int kKvWaves = 4;
+constexpr int kKvThreads = 64 * kKvWaves;
+constexpr int kKvBk = 32 * kKvWaves;  // keys per workgroup
+constexpr int kKvBq = 64;             // queries per tile
+
+template <int BYTES>
+struct QSlot {
+  __attribute__((aligned(1024))) uint8_t q[BYTES];
+  __attribute__((aligned(1024))) uint8_t g[BYTES];
+  // [0, 256): -LSE*log2(e) of the tile's 64 rows; [256, 512): D. Each copy
+  // writes 1 KiB, the rest of each half is padding.
+  __attribute__((aligned(1024))) float st[512];
+};
+
+template <Elt IN, int D, bool CAUSAL>
+__global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv(BwdArgs a) {
+  constexpr int ROWB = D * 2, TILE_B = kKvBq * ROWB;
+  constexpr int LPW = TILE_B / 1024 / kKvWaves;
+  constexpr int NS = kBwdStages;
+  constexpr int NKS = D / 16, NDB = D / 32;
+  constexpr int LOADS = 2 * LPW + 2;  // per wave per tile
+  static_assert(LPW >= 1, "tile too small for the wave count");
+
+  __shared__ QSlot<TILE_B> ring0, ring1, ring2, ring3;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 31, hl = lane >> 5;
+  const int n = a.n;
+  const int ktiles = (n + kKvBk - 1) / kKvBk;
+  // ascending key tiles: under a causal mask the first ones see the most queries
+  const TileId tl = tile_of_block(blockIdx.x, a.bh, ktiles, false);
+  const int k0 = tl.t * kKvBk;
+  const int kw0 = k0 + 32 * w;
+  const int key = kw0 + lr;
+  const size_t head_off = (size_t)tl.bh * (size_t)n * D;
+  const uint32_t head_bytes = (uint32_t)n * ROWB;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint8_t*)a.q + head_off * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint8_t*)a.k + head_off * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint8_t*)a.v + head_off * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc((const uint8_t*)a.dout + head_off * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.nlse2 + (size_t)tl.bh * n, (uint32_t)n * 4);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.delta + (size_t)tl.bh * n, (uint32_t)n * 4);
+
+  const int i_lo = CAUSAL ? k0 / kKvBq : 0;  // query tiles i_lo .. nt-1
+  const int nt = (n + kKvBq - 1) / kKvBq;
+
+  uint32_t off[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int byte = (w * LPW + i) * 1024 + lane * 16;
+    const int row = byte / ROWB, p = (byte % ROWB) / 16;
+    off[i] = (uint32_t)(row * ROWB + (p ^ swz2<D>(row)) * 16);
+  }
+  // Every wave copies the statistics too (the same bytes), so that all waves
+  // issue the same number of loads per tile.
+  auto issue = [&](QSlot<TILE_B>& slot, int t) __attribute__((always_inline)) {
+    const bool in = t < nt;
+    const uint32_t base = in ? (uint32_t)t * TILE_B : 0x80000000u;
+    const uint32_t sbase = in ? (uint32_t)t * (kKvBq * 4) : 0x80000000u;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      lds_dma16(rq, slot.q + (w * LPW + i) * 1024, base + off[i]);
+      lds_dma16(rg, slot.g + (w * LPW + i) * 1024, base + off[i]);
+    }
+    lds_dma16(rl, (uint8_t*)slot.st, sbase + lane * 16);
+    lds_dma16(rd, (uint8_t*)(slot.st + 256), sbase + lane * 16);
+  };
+
+  // K and V of this lane's key as B operands (d-columns ks*16 + hl*8 .. +8).
+  u32x4_t kf[NKS], vf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const uint32_t o_ = ((uint32_t)key * D + ks * 16 + hl * 8) * 2;
+    kf[ks] = bload16(rk, o_);
+    vf[ks] = bload16(rv, o_);
+  }
+  wait_vmcnt<0>();
+
+  const int qr = perm32(lr);
+  const int sw_r = swz2<D>(qr);
+  const int grp = lane >> 4, li = lane & 15;
+  const int trow = 8 * hl + (li >> 2);
+  const int sw_lo = swz2<D>(trow), sw_hi = swz2<D>(trow + 4);
+  const int tcol = 16 * (grp & 1) + 4 * (li & 3);
+
+  const float c = a.c;
+  f32x16_t dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = f32x16_t{};
+  const bool wave_live = kw0 < n;
+  auto live = [&](int i) __attribute__((always_inline)) {
+    return wave_live && !(CAUSAL && i * kKvBq + kKvBq - 1 < kw0);
+  };
+  auto needs_mask = [&](int i) __attribute__((always_inline)) {
+    return (kw0 + 31 >= n) || (CAUSAL && i * kKvBq < kw0 + 31);
+  };
+
+  auto compute = [&](const QSlot<TILE_B>& slot, int it) __attribute__((always_inline)) {
+    const bool mask = needs_mask(it);
+#pragma unroll
+    for (int qb = 0; qb < kKvBq / 32; ++qb) {
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+      const int row = qb * 32 + qr;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int at = row * ROWB + (((2 * ks + hl) ^ sw_r) * 16);
+        s = mfma16<IN>(*(const u32x4_t*)(slot.q + at), kf[ks], s);
+        dp = mfma16<IN>(*(const u32x4_t*)(slot.g + at), vf[ks], dp);
+      }
+      // register i holds query qb*32 + 8*hl + i (i < 8) or qb*32 + 16 + 8*hl + i - 8
+      float nl[16], dd[16];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int q_ = qb * 32 + 16 * h + 8 * hl + 4 * e;
+          const u32x4_t x = *(const u32x4_t*)(slot.st + q_);
+          const u32x4_t y = *(const u32x4_t*)(slot.st + 256 + q_);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            nl[8 * h + 4 * e + r] = __uint_as_float(x[r]);
+            dd[8 * h + 4 * e + r] = __uint_as_float(y[r]);
+          }
+        }
+      }
+      if (mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q_ = it * kKvBq + qb * 32 + 16 * (r >> 3) + 8 * hl + (r & 7);
+          const bool ok = key < n && (!CAUSAL || key <= q_);
+          s[r] = ok ? s[r] : -INFINITY;
+        }
+      }
+      u32x4_t pb[2], dsb[2];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[r], c, nl[r]));
+        const float p1 = fast_exp2(__builtin_fmaf(s[r + 1], c, nl[r + 1]));
+        pb[r >> 3][(r & 7) >> 1] = pack2<IN>(p0, p1);
+        dsb[r >> 3][(r & 7) >> 1] = pack2<IN>(p0 * (dp[r] - dd[r]), p1 * (dp[r + 1] - dd[r + 1]));
+      }
+      // dV^T += dO^T P,  dK^T += Q^T dS
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int r = qb * 32 + 16 * s2 + trow;
+          const int col = db * 32 + tcol;
+          const int half = (col & 4) << 1;
+          const int at_lo = r * ROWB + (((col >> 3) ^ sw_lo) * 16) + half;
+          const int at_hi = (r + 4) * ROWB + (((col >> 3) ^ sw_hi) * 16) + half;
+          const u32x2_t glo = lds_read_tr16(slot.g + at_lo);
+          const u32x2_t ghi = lds_read_tr16(slot.g + at_hi);
+          dv[db] = mfma16<IN>(u32x4_t{glo[0], glo[1], ghi[0], ghi[1]}, pb[s2], dv[db]);
+          const u32x2_t qlo = lds_read_tr16(slot.q + at_lo);
+          const u32x2_t qhi = lds_read_tr16(slot.q + at_hi);
+          dk[db] = mfma16<IN>(u32x4_t{qlo[0], qlo[1], qhi[0], qhi[1]}, dsb[s2], dk[db]);
+        }
+      }
+    }
+  };
+
+  auto slot_ref = [&](auto S) __attribute__((always_inline)) -> QSlot<TILE_B>& {
+    if constexpr (decltype(S)::value == 0) return ring0;
+    else if constexpr (decltype(S)::value == 1) return ring1;
+    else if constexpr (decltype(S)::value == 2) return ring2;
+    else return ring3;
+  };
+  auto step = [&](auto S, int i) __attribute__((always_inline)) {
+    using SN = std::integral_constant<int, (decltype(S)::value + NS - 1) % NS>;
+    wait_vmcnt<(NS - 2) * LOADS>();
+    __syncthreads();
+    issue(slot_ref(SN{}), i + NS - 1);
+    if (live(i)) compute(slot_ref(S), i);
+  };
+
+  {
+    QSlot<TILE_B>* slots[4] = {&ring0, &ring1, &ring2, &ring3};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      u32x4_t* p = (u32x4_t*)slots[s];
+      for (int i = tid; i < (int)(sizeof(QSlot<TILE_B>) / 16); i += kKvThreads) p[i] = u32x4_t{0, 0, 0, 0};
+    }
+  }
+  __syncthreads();
+
+  issue(ring0, i_lo);
+  issue(ring1, i_lo + 1);
+  issue(ring2, i_lo + 2);
+  for (int i0 = i_lo; i0 < nt; i0 += NS) {
+    step(std::integral_constant<int, 0>{}, i0);
+    if (i0 + 1 < nt) step(std::integral_constant<int, 1>{}, i0 + 1);
+    if (i0 + 2 < nt) step(std::integral_constant<int, 2>{}, i0 + 2);
+    if (i0 + 3 < nt) step(std::integral_constant<int, 3>{}, i0 + 3);
+  }
+  wait_vmcnt<0>();
+
+  if (key < n) {
+    store_rows<IN, NDB>((uint16_t*)a.dv + head_off + (size_t)key * D, hl, dv, 1.0f);
+    store_rows<IN, NDB>((uint16_t*)a.dk + head_off + (size_t)key * D, hl, dk, a.scale);
+  }
+}
+
+template <Elt E, int D>
+hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
+  const unsigned g1 = (unsigned)a.bh * (unsigned)((a.n + kDqBq - 1) / kDqBq);
+  const unsigned g2 = (unsigned)a.bh * (unsigned)((a.n + kKvBk - 1) / kKvBk);
+  if (a.causal) {
+    hipLaunchKernelGGL((bwd_dq<E, D, true>), dim3(g1), dim3(kDqThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv<E, D, true>), dim3(g2), dim3(kKvThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((bwd_dq<E, D, false>), dim3(g1), dim3(kDqThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv<E, D, false>), dim3(g2), dim3(kKvThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
+  if (a.elt == Elt::F16)
+    return a.d == 64 ? launch_bwd_t<Elt::F16, 64>(a, stream) : launch_bwd_t<Elt::F16, 128>(a, stream);
+  return a.d == 64 ? launch_bwd_t<Elt::BF16, 64>(a, stream) : launch_bwd_t<Elt::BF16, 128>(a, stream);
+}
+
+}  // namespace fa

@@ -41,49 +41,15 @@
 
 #include <type_traits>
 
+#include "fa_device.h"
 #include "fa_kernels.h"
 
 namespace fa {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBq = 32 * kWaves;  // query rows per workgroup
-constexpr float kLn2 = 0.693147180559945309f;
-
-struct TileId {
-  int bh;
-  int t;
-};
-
-// Workgroup id -> (batch*head, query tile).
-__device__ inline TileId tile_of_block(int pid, int bh_count, int tiles, bool causal) {
-  int bh, tt;
-  if ((bh_count & 7) == 0) {
-    const int xcd = pid & 7, slot = pid >> 3, per = bh_count >> 3;
-    tt = slot / per;
-    bh = xcd * per + slot % per;
-  } else {
-    tt = pid / bh_count;
-    bh = pid % bh_count;
-  }
-  return {bh, causal ? tiles - 1 - tt : tt};
-}
-
-// Accumulator row m of S^T holds key perm32(m) of the 32-key block.
-__device__ inline int perm32(int m) {
-  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
-}
-
-__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Key tiles [lo, hi) of this workgroup: its block of keys (grid dimension y),
 // cut at the last query row of the tile under a causal mask.
@@ -128,28 +94,6 @@ __device__ inline void store_partial(const FwdArgs& a, int bh, int qrow, int hl,
   if (hl == 0) a.part_lse[row] = lt > 0.f ? (m2 + __log2f(lt)) * kLn2 : -INFINITY;
 }
 
-template <Elt E>
-__device__ inline uint32_t pack2(float a, float b) {
-  if constexpr (E == Elt::F16) {
-    f16x2_t h = {(_Float16)a, (_Float16)b};
-    return __builtin_bit_cast(uint32_t, h);
-  } else {
-    bf16x2_t h = {(__bf16)a, (__bf16)b};
-    return __builtin_bit_cast(uint32_t, h);
-  }
-}
-
-// o += a * b on the 32x32x16 MFMA with 16-bit operands (F16 or BF16).
-template <Elt E>
-__device__ inline f32x16_t mfma16(u32x4_t a, u32x4_t b, f32x16_t c) {
-  if constexpr (E == Elt::F16)
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
-                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
 // Two OCP e4m3 codes (bytes 0,1 or, with HI, bytes 2,3 of w) -> two bf16,
 // exactly (every e4m3 value is a bf16 value).
 template <bool HI>
@@ -187,35 +131,6 @@ constexpr float kLazy = 8.0f;
 #ifndef FA_WAVES_PER_SIMD
 #define FA_WAVES_PER_SIMD 2
 #endif
-
-// x of this lane and of lane ^ 32, in an order that is the same on both lanes.
-struct PairVals {
-  float a, b;
-};
-__device__ inline PairVals pair_vals(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
-}
-__device__ inline float pair_max(float x) {
-  const PairVals p = pair_vals(x);
-  return fmaxf(p.a, p.b);
-}
-__device__ inline float pair_sum(float x) {
-  const PairVals p = pair_vals(x);
-  return p.a + p.b;
-}
-
-// Buffer resource over [base, base + bytes): loads at offsets past the end
-// return zeros, which pads ragged tiles without branches.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ inline u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ inline u32x2_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-}
 
 template <Elt IN, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads)
@@ -553,31 +468,6 @@ struct LdsSlot {
   __attribute__((aligned(1024))) uint8_t k[BYTES];
   __attribute__((aligned(1024))) uint8_t v[BYTES];
 };
-
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-
-__device__ inline u32x2_t lds_read_tr16(const uint8_t* p) {
-  const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4_t*)(p));
-  return __builtin_bit_cast(u32x2_t, r);
-}
-
-// One 16-byte buffer load per lane straight into LDS: lane i writes
-// lds + 16 * i. lds must be the same for the whole wave (it goes to M0).
-__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint8_t* lds, uint32_t voffset) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voffset), "s"(rsrc), "{m0}"(m0)
-               : "memory");
-}
-
-// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
-template <int N>
-__device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
 
 template <Elt IN, int D, bool CAUSAL>
 __global__ __launch_bounds__(kDirectThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -984,7 +874,6 @@ constexpr int kCombineRows = 256 / (D / 4);
 
 template <Elt OUT, int D>
 __global__ __launch_bounds__(256) void combine_splits(CombineArgs a) {
-  constexpr float kLog2e = 1.44269504088896340736f;
   constexpr int kLanesPerRow = D / 4;
   const int row = blockIdx.x * kCombineRows<D> + (int)threadIdx.x / kLanesPerRow;
   const int col = ((int)threadIdx.x % kLanesPerRow) * 4;

@@ -45,9 +45,35 @@ struct CombineArgs {
   Elt out;         // F32, F16 or BF16
 };
 
+// Backward pass (f16 / bf16): gradients of O = softmax(scale Q K^T + mask) V
+// given dO, recomputing P from Q, K and the forward's LSE.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;   // natural-log LSE of the forward, fp32 [bh][n]
+  float* delta;       // workspace: D = rowsum(dO * O), fp32 [bh][n]
+  float* nlse2;       // workspace: -LSE * log2(e), fp32 [bh][n]
+  void* dq;
+  void* dk;
+  void* dv;
+  int bh;
+  int n;
+  int d;
+  bool causal;
+  float c;            // scale * log2(e)
+  float scale;
+  Elt elt;            // F16 or BF16
+};
+
 // Enqueue the forward kernel for validated arguments. Returns the HIP status
 // of the launch.
 hipError_t launch_forward(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+// Enqueue the two backward kernels (the query-major dQ pass, which also
+// writes delta and nlse2, then the key-major dK / dV pass).
+hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace fa

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the attention forward pass.
+"""Seeded synthetic inputs for the attention forward and backward passes.
 
 This module only draws and encodes inputs; it holds none of the attention
 arithmetic. Both the HIP path (through its binding) and the CPU oracle
@@ -13,6 +13,9 @@ Recipe (the same for every configuration):
   * an optional multiplier per tensor (the fp8 workload scales Q and K by 4
     so that raw scores reach large magnitudes);
   * a cast to the storage dtype with round-to-nearest-even.
+
+For the backward pass the output gradient dO is the fourth draw of the same
+generator (after Q, K, V), of the same shape, N(0,1), cast the same way.
 
 For fp8 (OCP e4m3fn, largest finite value 448) each tensor gets one fp32
 descale s = amax(|x|) / 448; the stored code is x / s clamped to [-448, 448]
@@ -132,6 +135,17 @@ def make_inputs(batch: int, heads: int, n: int, d_k: int, dtype: str, seed: int,
         return Inputs(q8, k8, v8, dtype, qs, ks, vs)
     td = _TORCH_DTYPE[dtype]
     return Inputs(q.to(td), k.to(td), v.to(td), dtype)
+
+
+def make_inputs_with_grad(batch: int, heads: int, n: int, d_k: int, dtype: str, seed: int):
+    """Q, K, V as ``make_inputs`` plus dO, the generator's fourth draw (f16 / bf16 / f32)."""
+    if dtype not in ("f32", "f16", "bf16"):
+        raise ValueError("the backward inputs are f32, f16 or bf16")
+    g = torch.Generator().manual_seed(int(seed))
+    shape = (batch, heads, n, d_k)
+    td = _TORCH_DTYPE[dtype]
+    q, k, v, do = (torch.randn(shape, generator=g, dtype=torch.float32).to(td) for _ in range(4))
+    return Inputs(q, k, v, dtype), do
 
 
 def workload_inputs(w: Workload, seed: int) -> Inputs:
