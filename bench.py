@@ -11,7 +11,9 @@ HBM traffic measured by rocprofv3 counters when the stored measurement
 belongs to the current kernel source) and the CPU oracle timed on a bounded
 sample of the same workload on this host's cores.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--splits S] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--n N] [--splits S] [--no-cpu-baseline]
+    python bench.py --backward      # fa_backward on the workload
+    python bench.py --unfused       # the unfused contrast (S, P in memory)
     python bench.py --copy-calibration      # plain copy of known size (counter scale)
 """
 from __future__ import annotations
@@ -38,6 +40,7 @@ KERNEL_OF_DTYPE = {"bf16": "fwd_direct", "f16": "fwd_direct", "fp8": "fwd_mfma16
 # the files the forward kernels and their launch shape are compiled from; a
 # stored traffic measurement is valid only for the sources it was taken on
 KERNEL_SOURCES = ("transformer_attention_08_amd/csrc/fa_fwd.hip",
+                  "transformer_attention_08_amd/csrc/fa_device.h",
                   "transformer_attention_08_amd/csrc/fa_kernels.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama3_8b_bf16_causal.json")
 
@@ -206,6 +209,9 @@ def main(argv=None):
                     help="cut the keys into this many blocks (fa_forward_splitkv) and merge")
     ap.add_argument("--backward", action="store_true",
                     help="time fa_backward (dQ, dK, dV) instead of the forward")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the unfused contrast (S and P written to memory) instead")
+    ap.add_argument("--n", type=int, default=0, help="override the workload's sequence length")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args(argv)
@@ -226,6 +232,9 @@ def main(argv=None):
     import workload
 
     w = workload.WORKLOADS[args.workload]
+    if args.n:
+        import dataclasses
+        w = dataclasses.replace(w, name=f"{w.name}_n{args.n}", n=args.n)
     fa.load_library()
     if args.backward:
         return bench_backward(args, w)
@@ -243,8 +252,18 @@ def main(argv=None):
         need = fa.splitkv_workspace_size(w.batch, w.heads, w.n, w.d_k, args.splits)
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
 
+    uws = None
+    if args.unfused:
+        if w.dtype not in ("bf16", "f16"):
+            print("the unfused contrast runs on f16 / bf16 workloads", file=sys.stderr)
+            return 2
+        uws = torch.empty(fa.unfused_workspace_size(w.batch, w.heads, w.n), dtype=torch.uint8, device=dev)
+
     def step():
-        if ws is not None:
+        if uws is not None:
+            fa.forward_unfused(d.q, d.k, d.v, causal=w.causal, scale=w.scale, out=o, lse=lse,
+                               workspace=uws)
+        elif ws is not None:
             fa.forward_splitkv(d.q, d.k, d.v, args.splits, causal=w.causal, scale=w.scale, out=o,
                                lse=lse, workspace=ws)
         elif w.dtype == "fp8":
@@ -275,10 +294,12 @@ def main(argv=None):
     peak = PEAK_TFLOPS[w.dtype]
     traffic = stored_traffic(w.name)
     split_tag = f", split-KV {args.splits}" if ws is not None else ""
-    if ws is not None:
-        traffic = None  # the stored counters cover the unsplit kernel only
+    if uws is not None:
+        split_tag = ", unfused: S and P in memory"
+    if ws is not None or uws is not None or args.n:
+        traffic = None  # the stored counters cover the fused kernel at the stored shape only
     line = {
-        "metric": (METRIC if w.name == "llama3_8b_bf16_causal" and ws is None
+        "metric": (METRIC if w.name == "llama3_8b_bf16_causal" and ws is None and uws is None
                    else f"attn fwd TFLOP/s ({w.name}{split_tag})"),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
@@ -298,7 +319,8 @@ def main(argv=None):
         "ms_min": round(min(per), 5),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": traffic,
-                     "kernel": KERNEL_OF_DTYPE[w.dtype] + ("+combine_splits" if ws is not None else ""),
+                     "kernel": ("unf_scores+unf_softmax+unf_pv" if uws is not None else
+                                KERNEL_OF_DTYPE[w.dtype] + ("+combine_splits" if ws is not None else "")),
                      "min_hbm_bytes": min_hbm_bytes(w)},
     }
     if not args.no_cpu_baseline:

@@ -185,6 +185,30 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
 /* Workspace bytes fa_backward needs (0 for invalid sizes). Pure host code. */
 size_t fa_backward_workspace_size(int batch, int heads, int n);
 
+/*
+ * fa_forward_unfused -- the same O and LSE as fa_forward (f16 / bf16), computed
+ * step by step with S and P written to memory: S = scale Q K^T (causal
+ * entries -inf) as fp32, then a row softmax writing P in the input type and
+ * LSE, then O = P V. This is the computation the fused kernel replaces
+ * (slides "Case study: FlashAttention", slide "FlashAttention: the idea":
+ * done step by step, S and P go out to HBM and back); it exists as a measured
+ * contrast, not as a fast path. Its memory traffic and workspace grow as n^2.
+ *
+ *   workspace   caller-owned device memory, 16-byte aligned, at least
+ *               fa_unfused_workspace_size(batch, heads, n) bytes: fp32 S
+ *               [batch, heads, n, n] from byte 0, P [batch, heads, n, n] in
+ *               the input type from the next multiple of 256 bytes; on return
+ *               it holds S and P
+ * Other arguments as fa_forward. dtype must be FA_F16 or FA_BF16
+ * (FA_ERR_UNSUPPORTED otherwise). Three kernels are enqueued on `stream`.
+ */
+int fa_forward_unfused(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int batch, int heads, int n, int d_k, float scale, int causal, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fa_forward_unfused needs (0 for invalid sizes). */
+size_t fa_unfused_workspace_size(int batch, int heads, int n);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_string(int status);
 

@@ -207,3 +207,31 @@ def test_backward_inputs_may_alias_each_other(lib):
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="needs a host without a visible GPU")
 def test_backward_valid_call_without_gpu_reports_hip_error(lib):
     assert bcall(lib) == 9
+
+
+# ---------------------------------------------------------------- unfused contrast
+
+def test_unfused_workspace_size(lib):
+    for b, h, n in ((1, 1, 1), (2, 3, 100), (1, 32, 8192)):
+        cells = b * h * n * n
+        assert lib.fa_unfused_workspace_size(b, h, n) == -(-cells * 4 // 256) * 256 + cells * 2
+    assert lib.fa_unfused_workspace_size(1, 0, 10) == 0
+
+
+def test_unfused_validation(lib):
+    W = BASE + 20 * SPAN
+
+    def c(ws=W, wsb=1 << 30, **kw):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, b=1, h=2, n=100, d=128, scale=0.125, causal=1, dtype=2)
+        a.update(kw)
+        return lib.fa_forward_unfused(a["q"], a["k"], a["v"], a["o"], a["lse"], a["b"], a["h"], a["n"],
+                                      a["d"], a["scale"], a["causal"], a["dtype"], ws, wsb, None)
+    assert c(n=0) == 2
+    assert c(dtype=0) == 4 and c(dtype=3) == 4
+    assert c(ws=None) == 1
+    assert c(ws=W + 8) == 5
+    need = lib.fa_unfused_workspace_size(1, 2, 100)
+    assert c(wsb=need - 1) == 2
+    assert c(ws=Q) == 7 and c(ws=L - 64) == 7
+    if torch.cuda.device_count() == 0:
+        assert c() == 9

@@ -34,7 +34,8 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_DTYPE",
           8: "FA_ERR_OVERFLOW", 9: "FA_ERR_HIP"}
 
 EXPORTS = ("fa_forward", "fa_forward_fp8", "fa_forward_splitkv", "fa_splitkv_workspace_size",
-           "fa_backward", "fa_backward_workspace_size", "fa_status_string", "fa_last_hip_error",
+           "fa_backward", "fa_backward_workspace_size", "fa_forward_unfused",
+           "fa_unfused_workspace_size", "fa_status_string", "fa_last_hip_error",
            "fa_abi_version")
 
 _lib = None
@@ -69,6 +70,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_backward.restype = i
     lib.fa_backward_workspace_size.argtypes = [i, i, i]
     lib.fa_backward_workspace_size.restype = sz
+    lib.fa_forward_unfused.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.fa_forward_unfused.restype = i
+    lib.fa_unfused_workspace_size.argtypes = [i, i, i]
+    lib.fa_unfused_workspace_size.restype = sz
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_hip_error.argtypes = []
@@ -225,3 +230,28 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                          _stream(q.device))
     _check(st)
     return dq, dk, dv
+
+
+def unfused_workspace_size(batch: int, heads: int, n: int) -> int:
+    """Bytes of workspace ``forward_unfused`` needs (S fp32 plus P, n x n per head)."""
+    return int(load_library().fa_unfused_workspace_size(batch, heads, n))
+
+
+def forward_unfused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                    scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """``fa_forward_unfused``: O and LSE computed with S and P materialised.
+    Returns (O, LSE, workspace); the workspace holds S (fp32) and P after the call."""
+    lib = load_library()
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("forward_unfused takes float16 or bfloat16 tensors")
+    out, lse = _prepare(q, k, v, out, lse)
+    b, h, n, d = q.shape
+    if workspace is None:
+        workspace = torch.empty(unfused_workspace_size(b, h, n), dtype=torch.uint8, device=q.device)
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib.fa_forward_unfused(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, h, n, d, s,
+                                1 if causal else 0, _DTYPE_CODE[q.dtype], _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(st)
+    return out, lse, workspace

@@ -142,6 +142,19 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
   return FA_OK;
 }
 
+// Unfused workspace: fp32 S [bh][n][n] at byte 0, P in the input type from
+// the next multiple of 256 bytes.
+struct UnfLayout {
+  size_t p_off, total;
+};
+UnfLayout unf_layout(int batch, int heads, int n) {
+  const size_t cells = (size_t)batch * heads * (size_t)n * (size_t)n;
+  UnfLayout l;
+  l.p_off = (cells * 4 + 255) / 256 * 256;
+  l.total = l.p_off + cells * 2;
+  return l;
+}
+
 int run(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int heads,
         int n, int d_k, float qk_scale, int causal, int dtype, float o_mult, void* stream,
         int splits = 1, void* workspace = nullptr) {
@@ -257,6 +270,58 @@ int fa_forward_splitkv(const void* q, const void* k, const void* v, void* o, flo
   }
   return run(q, k, v, o, lse, batch, heads, n, d_k, scale, causal, dtype, 1.0f, stream, splits,
              workspace);
+}
+
+size_t fa_unfused_workspace_size(int batch, int heads, int n) {
+  if (batch < 1 || heads < 1 || n < 1) return 0;
+  if ((double)batch * heads * (double)n * n * 6.0 > 9.0e18) return 0;
+  return unf_layout(batch, heads, n).total;
+}
+
+int fa_forward_unfused(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                       int heads, int n, int d_k, float scale, int causal, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = validate(q, k, v, o, lse, batch, heads, n, d_k, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (!workspace) return FA_ERR_NULL;
+  if ((uintptr_t)workspace % 16) return FA_ERR_ALIGN;
+  if ((double)batch * heads * (double)n * n * 6.0 > 9.0e18) return FA_ERR_OVERFLOW;
+  const UnfLayout ul = unf_layout(batch, heads, n);
+  if (workspace_bytes < ul.total) return FA_ERR_SHAPE;
+  const int64_t rows = (int64_t)batch * heads * n;
+  const uintptr_t t_sz = (uintptr_t)(rows * d_k * 2);
+  const Range rw{(uintptr_t)workspace, (uintptr_t)workspace + ul.total};
+  const Range others[4] = {{(uintptr_t)q, (uintptr_t)q + t_sz}, {(uintptr_t)k, (uintptr_t)k + t_sz},
+                           {(uintptr_t)v, (uintptr_t)v + t_sz}, {(uintptr_t)o, (uintptr_t)o + t_sz}};
+  for (const Range& r : others)
+    if (overlap(rw, r)) return FA_ERR_ALIAS;
+  if (lse && overlap(rw, Range{(uintptr_t)lse, (uintptr_t)lse + (uintptr_t)(rows * 4)})) return FA_ERR_ALIAS;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) {
+    fa::UnfArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.s = (float*)workspace;
+    a.p = (uint16_t*)((char*)workspace + ul.p_off);
+    a.bh = batch * heads;
+    a.n = n;
+    a.d = d_k;
+    a.rows = (int)rows;
+    a.causal = causal != 0;
+    a.scale = scale;
+    a.elt = static_cast<fa::Elt>(dtype);
+    e = fa::launch_unfused(a, static_cast<hipStream_t>(stream));
+  }
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
 }
 
 size_t fa_backward_workspace_size(int batch, int heads, int n) {

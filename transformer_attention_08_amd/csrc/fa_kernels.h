@@ -3,6 +3,8 @@
 // include/fa.h.
 #pragma once
 
+#include <stdint.h>
+
 #include <hip/hip_runtime_api.h>
 
 namespace fa {
@@ -68,6 +70,25 @@ struct BwdArgs {
   Elt elt;            // F16 or BF16
 };
 
+// Unfused forward (f16 / bf16): S and P materialised in the caller's
+// workspace.
+struct UnfArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;      // may be null
+  float* s;        // fp32 S [bh][n][n]
+  uint16_t* p;     // P in the input type [bh][n][n]
+  int bh;
+  int n;
+  int d;
+  int rows;        // bh * n
+  bool causal;
+  float scale;
+  Elt elt;
+};
+
 // Enqueue the forward kernel for validated arguments. Returns the HIP status
 // of the launch.
 hipError_t launch_forward(const FwdArgs& a, hipStream_t stream);
@@ -75,5 +96,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 // Enqueue the two backward kernels (the query-major dQ pass, which also
 // writes delta and nlse2, then the key-major dK / dV pass).
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
+// Enqueue the three unfused kernels (scores, row softmax, P V).
+hipError_t launch_unfused(const UnfArgs& a, hipStream_t stream);
 
 }  // namespace fa
