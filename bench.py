@@ -14,6 +14,8 @@ sample of the same workload on this host's cores.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--n N] [--splits S] [--no-cpu-baseline]
     python bench.py --backward      # fa_backward on the workload
     python bench.py --unfused       # the unfused contrast (S, P in memory)
+    python bench.py --layout bshd   # [batch, n, heads, d_k] inputs (fa_forward_strided)
+    python bench.py --varlen 16     # a ragged batch of 16 sequences (fa_forward_varlen)
     python bench.py --copy-calibration      # plain copy of known size (counter scale)
 """
 from __future__ import annotations
@@ -198,6 +200,67 @@ def bench_backward(args, w):
     return 0
 
 
+def varlen_lengths(count: int, n_max: int, seed: int):
+    """Seeded log-normal sequence lengths in [16, n_max] (median about n_max / 5)."""
+    import numpy as np
+    rng = np.random.default_rng(seed + 7)
+    mu = math.log(max(16, n_max // 5))
+    return np.clip(np.exp(rng.normal(mu, 1.0, count)).astype(int), 16, n_max).tolist()
+
+
+def bench_varlen(args, w):
+    """One step = one fa_forward_varlen call over a packed batch of sequences
+    of mixed lengths with the workload's heads, d_k, dtype and mask."""
+    import numpy as np
+    import torch
+
+    import transformer_attention_08_amd as fa
+    import workload
+
+    lens = varlen_lengths(args.varlen, w.n, args.seed)
+    total = int(sum(lens))
+    if w.dtype == "fp8":
+        print("the ragged-batch bench runs on f32 / f16 / bf16 workloads", file=sys.stderr)
+        return 2
+    inp = workload.make_inputs(1, w.heads, total, w.d_k, w.dtype, args.seed)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = (t[0].transpose(0, 1).contiguous().to(dev) for t in (inp.q, inp.k, inp.v))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.heads, total), dtype=torch.float32, device=dev)
+
+    def step():
+        fa.forward_varlen(q, k, v, cu, max(lens), causal=w.causal, scale=w.scale, out=o, lse=lse)
+
+    ms, per = time_steps(step, torch.cuda.current_stream(dev), args.steps, args.warmup)
+    flops = sum(4.0 * w.heads * x * x * w.d_k / (2 if w.causal else 1) for x in lens)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    line = {
+        "metric": f"attn fwd TFLOP/s ({w.name}, ragged batch of {len(lens)})",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs; seeded log-normal sequence lengths)",
+        "config": {"workload": w.name + "_varlen", "heads": w.heads, "d_k": w.d_k, "causal": w.causal,
+                   "lengths": lens, "total_rows": total, "flops_per_step": flops},
+        "pct_of_peak": round(100.0 * tflops / peak, 2),
+        "ms_median": round(statistics.median(per), 5),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": None, "kernel": KERNEL_OF_DTYPE[w.dtype]},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,6 +275,11 @@ def main(argv=None):
     ap.add_argument("--unfused", action="store_true",
                     help="time the unfused contrast (S and P written to memory) instead")
     ap.add_argument("--n", type=int, default=0, help="override the workload's sequence length")
+    ap.add_argument("--layout", choices=("bhsd", "bshd"), default="bhsd",
+                    help="bshd: q, k, v, o as [batch, n, heads, d_k] through fa_forward_strided")
+    ap.add_argument("--varlen", type=int, default=0,
+                    help="ragged batch of this many sequences (seeded log-normal lengths, "
+                         "16 .. n rows) through fa_forward_varlen")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args(argv)
@@ -238,6 +306,8 @@ def main(argv=None):
     fa.load_library()
     if args.backward:
         return bench_backward(args, w)
+    if args.varlen:
+        return bench_varlen(args, w)
     inp = workload.workload_inputs(w, args.seed)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -252,6 +322,9 @@ def main(argv=None):
         need = fa.splitkv_workspace_size(w.batch, w.heads, w.n, w.d_k, args.splits)
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
 
+    if args.layout == "bshd":
+        qs, ks, vs = (t.transpose(1, 2).contiguous() for t in (d.q, d.k, d.v))
+        os_ = torch.empty((w.batch, w.n, w.heads, w.d_k), dtype=o.dtype, device=dev)
     uws = None
     if args.unfused:
         if w.dtype not in ("bf16", "f16"):
@@ -260,7 +333,9 @@ def main(argv=None):
         uws = torch.empty(fa.unfused_workspace_size(w.batch, w.heads, w.n), dtype=torch.uint8, device=dev)
 
     def step():
-        if uws is not None:
+        if args.layout == "bshd":
+            fa.forward_strided(qs, ks, vs, layout="bshd", causal=w.causal, scale=w.scale, out=os_, lse=lse)
+        elif uws is not None:
             fa.forward_unfused(d.q, d.k, d.v, causal=w.causal, scale=w.scale, out=o, lse=lse,
                                workspace=uws)
         elif ws is not None:
@@ -296,10 +371,13 @@ def main(argv=None):
     split_tag = f", split-KV {args.splits}" if ws is not None else ""
     if uws is not None:
         split_tag = ", unfused: S and P in memory"
-    if ws is not None or uws is not None or args.n:
+    if args.layout == "bshd":
+        split_tag += ", [b, n, h, d_k] layout"
+    if ws is not None or uws is not None or args.n or args.layout != "bhsd":
         traffic = None  # the stored counters cover the fused kernel at the stored shape only
     line = {
         "metric": (METRIC if w.name == "llama3_8b_bf16_causal" and ws is None and uws is None
+                   and args.layout == "bhsd"
                    else f"attn fwd TFLOP/s ({w.name}{split_tag})"),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
@@ -313,7 +391,8 @@ def main(argv=None):
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "n": w.n, "d_k": w.d_k,
-                   "causal": w.causal, "flops_per_step": flops, "splits": args.splits},
+                   "causal": w.causal, "flops_per_step": flops, "splits": args.splits,
+                   "layout": args.layout},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "ms_median": round(statistics.median(per), 5),
         "ms_min": round(min(per), 5),

@@ -56,6 +56,7 @@
 #define FA_MI355X_FA_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -110,6 +111,47 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                    int batch, int heads, int n, int d_k, float scale, int causal,
                    float q_descale, float k_descale, float v_descale, void* stream);
+
+/*
+ * fa_forward_strided -- fa_forward on q, k, v, o laid out with arbitrary
+ * element strides (d_k contiguous): element (b, h, i, c) of q is
+ *     q[b * strides[0] + h * strides[1] + i * strides[2] + c]
+ * and likewise k (strides[3..5]), v (strides[6..8]) and o (strides[9..11]).
+ * This takes, for example, the [batch, n, heads, d_k] rows of X Wq directly,
+ * without the head transpose of the slide "Queries, keys and values" (strides
+ * n*heads*d_k, d_k, heads*d_k). lse stays dense [batch, heads, n]. The result
+ * is bitwise the one fa_forward gives on the same values in the dense layout.
+ *   strides   12 int64 values (elements), each >= 0; a row stride must be
+ *             >= d_k (FA_ERR_UNSUPPORTED otherwise); each stride times the
+ *             element size must be a multiple of 16 bytes (FA_ERR_ALIGN); the
+ *             rows that o addresses must be disjoint (FA_ERR_ALIAS); one
+ *             head's rows must span less than 2^31 bytes (FA_ERR_OVERFLOW)
+ * Other arguments and errors as fa_forward (FA_FP8_E4M3: unit descales).
+ */
+int fa_forward_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int batch, int heads, int n, int d_k, const int64_t* strides,
+                       float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_forward_varlen -- fa_forward over a ragged batch: `batch` sequences of
+ * different lengths packed along one row axis. Sequence b is rows
+ * cu_seqlens[b] .. cu_seqlens[b+1] - 1; attention (and the causal mask, by
+ * position within the sequence) never crosses sequences.
+ *   q, k, v, o    [total, heads, d_k], contiguous (d_k fastest)
+ *   lse           [heads, total] fp32, or NULL
+ *   cu_seqlens    DEVICE pointer to batch + 1 int32 offsets, non-decreasing,
+ *                 cu_seqlens[0] = 0, cu_seqlens[batch] = total, and no
+ *                 sequence longer than max_seqlen. The kernels clamp every
+ *                 offset to [0, total] and every length to max_seqlen, so
+ *                 other contents give unspecified results but no access
+ *                 outside the arrays.
+ *   max_seqlen    the longest sequence (sizes the grid), >= 1
+ * total = 0 returns FA_OK without launching. Other arguments and errors as
+ * fa_forward (FA_FP8_E4M3: unit descales).
+ */
+int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const int* cu_seqlens, int batch, int total, int max_seqlen, int heads,
+                      int d_k, float scale, int causal, int dtype, void* stream);
 
 /*
  * fa_forward_splitkv -- fa_forward with the keys of every (batch, head) cut

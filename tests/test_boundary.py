@@ -235,3 +235,55 @@ def test_unfused_validation(lib):
     assert c(ws=Q) == 7 and c(ws=L - 64) == 7
     if torch.cuda.device_count() == 0:
         assert c() == 9
+
+
+# ---------------------------------------------------------------- strided and ragged layouts
+
+def scall(lib, strides=None, q=Q, k=K, v=V, o=O, lse=L, b=2, h=3, n=100, d=128, scale=0.125, causal=1,
+          dtype=2):
+    if strides is None:  # [b, n, h, d] for all four
+        strides = [n * h * d, d, h * d] * 4
+    arr = None if strides == "null" else (ctypes.c_int64 * 12)(*strides)
+    return lib.fa_forward_strided(q, k, v, o, lse, b, h, n, d, arr, scale, causal, dtype, None)
+
+
+def test_strided_validation(lib):
+    b, h, n, d = 2, 3, 100, 128
+    bshd = [n * h * d, d, h * d]
+    assert scall(lib, strides="null") == 1
+    assert scall(lib, n=0) == 2
+    assert scall(lib, d=96) == 4
+    assert scall(lib, strides=bshd * 3 + [n * h * d, d, 64]) == 4          # O rows overlap within a head
+    assert scall(lib, strides=[-1, d, h * d] + bshd * 3) == 4
+    assert scall(lib, strides=bshd * 3 + [n * h * d, 4, h * d]) == 5       # 8-byte stride
+    assert scall(lib, strides=bshd * 3 + [n * h * d, 64, h * d]) == 7     # heads of O overlap
+    assert scall(lib, strides=bshd * 3 + [0, d, h * d]) == 7              # batches of O overlap
+    assert scall(lib, strides=bshd[:2] + [1 << 22] + bshd * 3) == 8       # one head past 2^31 bytes
+    assert scall(lib, o=Q) == 7 and scall(lib, lse=V + 64) == 7
+    assert scall(lib, q=Q + 8) == 5
+
+
+def test_strided_rows_disjoint_accepts_common_layouts(lib):
+    b, h, n, d = 2, 3, 100, 128
+    if torch.cuda.device_count() == 0:
+        for s in ([h * n * d, n * d, d], [n * h * d, d, h * d], [h * n * 192, n * 192, 192]):
+            assert scall(lib, strides=s * 4) == 9   # valid: reaches the (absent) GPU
+
+
+def vcall(lib, q=Q, k=K, v=V, o=O, lse=L, cu=BASE + 30 * SPAN, batch=4, total=1000, maxlen=600, h=2,
+          d=128, scale=0.125, causal=1, dtype=2):
+    return lib.fa_forward_varlen(q, k, v, o, lse, cu, batch, total, maxlen, h, d, scale, causal, dtype,
+                                 None)
+
+
+def test_varlen_validation(lib):
+    C = BASE + 30 * SPAN
+    assert vcall(lib, cu=None) == 1 and vcall(lib, q=None) == 1
+    assert vcall(lib, batch=0) == 2 and vcall(lib, maxlen=0) == 2 and vcall(lib, total=-1) == 2
+    assert vcall(lib, dtype=7) == 3 and vcall(lib, d=32) == 4
+    assert vcall(lib, cu=C + 2) == 5 and vcall(lib, o=O + 8) == 5
+    assert vcall(lib, scale=float("inf")) == 6
+    assert vcall(lib, o=K + 128) == 7 and vcall(lib, cu=O + 64) == 7 and vcall(lib, lse=Q) == 7
+    assert vcall(lib, maxlen=1 << 20, h=32) == 8
+    # no rows: valid and nothing is launched, so no HIP call is made
+    assert vcall(lib, total=0) == 0

@@ -33,7 +33,8 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_DTYPE",
           4: "FA_ERR_UNSUPPORTED", 5: "FA_ERR_ALIGN", 6: "FA_ERR_SCALE", 7: "FA_ERR_ALIAS",
           8: "FA_ERR_OVERFLOW", 9: "FA_ERR_HIP"}
 
-EXPORTS = ("fa_forward", "fa_forward_fp8", "fa_forward_splitkv", "fa_splitkv_workspace_size",
+EXPORTS = ("fa_forward", "fa_forward_fp8", "fa_forward_strided", "fa_forward_varlen",
+           "fa_forward_splitkv", "fa_splitkv_workspace_size",
            "fa_backward", "fa_backward_workspace_size", "fa_forward_unfused",
            "fa_unfused_workspace_size", "fa_status_string", "fa_last_hip_error",
            "fa_abi_version")
@@ -74,6 +75,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_forward_unfused.restype = i
     lib.fa_unfused_workspace_size.argtypes = [i, i, i]
     lib.fa_unfused_workspace_size.restype = sz
+    lib.fa_forward_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp, f, i, i, vp]
+    lib.fa_forward_strided.restype = i
+    lib.fa_forward_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    lib.fa_forward_varlen.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_hip_error.argtypes = []
@@ -255,3 +260,75 @@ def forward_unfused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: b
                                 workspace.numel() * workspace.element_size(), _stream(q.device))
     _check(st)
     return out, lse, workspace
+
+
+def _head_strides(t: torch.Tensor, layout: str):
+    """(batch, head, row) element strides of a 4-D tensor in layout "bhsd" or "bshd"."""
+    if t.stride(-1) != 1:
+        raise ValueError("the last (d_k) dimension must be contiguous")
+    s = t.stride()
+    return (s[0], s[1], s[2]) if layout == "bhsd" else (s[0], s[2], s[1])
+
+
+def forward_strided(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str = "bshd",
+                    causal: bool = False, scale: Optional[float] = None,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    out_layout: Optional[str] = None):
+    """``fa_forward_strided``: q, k, v are 4-D device tensors (any strides, d_k
+    contiguous) indexed [batch, heads, n, d_k] ("bhsd") or [batch, n, heads,
+    d_k] ("bshd"). O is allocated in ``out_layout`` (default: ``layout``) unless
+    given. Returns (O, LSE [batch, heads, n])."""
+    lib = load_library()
+    if layout not in ("bhsd", "bshd"):
+        raise ValueError("layout is 'bhsd' or 'bshd'")
+    out_layout = out_layout or layout
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one 4-D shape and dtype")
+    if q.dtype not in _DTYPE_CODE or not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors of a supported dtype")
+    if layout == "bhsd":
+        b, h, n, d = q.shape
+    else:
+        b, n, h, d = q.shape
+    if out is None:
+        shape = (b, h, n, d) if out_layout == "bhsd" else (b, n, h, d)
+        out = torch.empty(shape, dtype=_OUT_DTYPE[q.dtype], device=q.device)
+    if lse is None:
+        lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+    st = [*_head_strides(q, layout), *_head_strides(k, layout), *_head_strides(v, layout),
+          *_head_strides(out, out_layout)]
+    arr = (ctypes.c_int64 * 12)(*st)
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    r = lib.fa_forward_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, h, n, d,
+                               ctypes.cast(arr, ctypes.c_void_p), s, 1 if causal else 0,
+                               _DTYPE_CODE[q.dtype], _stream(q.device))
+    _check(r)
+    return out, lse
+
+
+def forward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                   max_seqlen: int, causal: bool = False, scale: Optional[float] = None,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """``fa_forward_varlen``: q, k, v [total, heads, d_k] contiguous device tensors
+    holding packed sequences; cu_seqlens an int32 device tensor of batch + 1
+    offsets. Returns (O [total, heads, d_k], LSE [heads, total])."""
+    lib = load_library()
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one [total, heads, d_k] shape and dtype")
+    for t in (q, k, v, cu_seqlens):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous device tensors")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+    total, h, d = q.shape
+    batch = cu_seqlens.numel() - 1
+    if out is None:
+        out = torch.empty((total, h, d), dtype=_OUT_DTYPE[q.dtype], device=q.device)
+    if lse is None:
+        lse = torch.empty((h, total), dtype=torch.float32, device=q.device)
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    r = lib.fa_forward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens),
+                              batch, total, int(max_seqlen), h, d, s, 1 if causal else 0,
+                              _DTYPE_CODE[q.dtype], _stream(q.device))
+    _check(r)
+    return out, lse

@@ -155,9 +155,47 @@ UnfLayout unf_layout(int batch, int heads, int n) {
   return l;
 }
 
+// Element strides (batch, head, row) of q, k, v, o, and the ragged-batch
+// description; null in run() means the dense [batch, heads, n, d_k] layout.
+struct Layout {
+  int64_t s[12];
+  const int* cu_seqlens;
+  int total;
+};
+
+int elt_bytes_in(int dtype) { return dtype == FA_F32 ? 4 : dtype == FA_FP8_E4M3 ? 1 : 2; }
+int elt_bytes_out(int dtype) { return dtype == FA_F32 ? 4 : 2; }
+
+// Byte range [lo, hi) a strided tensor touches.
+Range strided_span(const void* p, const int64_t* s, int batch, int heads, int n, int d_k, int esize) {
+  const int64_t last = (int64_t)(batch - 1) * s[0] + (int64_t)(heads - 1) * s[1] + (int64_t)(n - 1) * s[2] + d_k;
+  return {(uintptr_t)p, (uintptr_t)p + (uintptr_t)(last * esize)};
+}
+
+// Do the (batch, head, row) positions of a strided tensor address disjoint
+// d_k-element rows? Sufficient test: sorted by stride, every dimension of
+// extent > 1 steps over the whole extent of the ones below it.
+bool rows_disjoint(const int64_t* s, int batch, int heads, int n, int d_k) {
+  int64_t st[3] = {s[0], s[1], s[2]};
+  int64_t ex[3] = {batch, heads, n};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (st[j] < st[i]) {
+        std::swap(st[i], st[j]);
+        std::swap(ex[i], ex[j]);
+      }
+  int64_t covered = d_k;  // elements spanned by the dimensions below
+  for (int i = 0; i < 3; ++i) {
+    if (ex[i] == 1) continue;
+    if (st[i] < covered) return false;
+    covered = st[i] * (ex[i] - 1) + covered;
+  }
+  return true;
+}
+
 int run(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int heads,
         int n, int d_k, float qk_scale, int causal, int dtype, float o_mult, void* stream,
-        int splits = 1, void* workspace = nullptr) {
+        int splits = 1, void* workspace = nullptr, const Layout* lay = nullptr) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) {
@@ -170,6 +208,14 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int ba
     a.bh = batch * heads;
     a.n = n;
     a.d = d_k;
+    a.heads = heads;
+    const int64_t dense[3] = {(int64_t)heads * n * d_k, (int64_t)n * d_k, d_k};
+    const int64_t* s = lay ? lay->s : nullptr;
+    int64_t* dst[12] = {&a.q_sb, &a.q_sh, &a.q_sr, &a.k_sb, &a.k_sh, &a.k_sr,
+                        &a.v_sb, &a.v_sh, &a.v_sr, &a.o_sb, &a.o_sh, &a.o_sr};
+    for (int i = 0; i < 12; ++i) *dst[i] = s ? s[i] : dense[i % 3];
+    a.cu_seqlens = lay ? lay->cu_seqlens : nullptr;
+    a.total = lay ? lay->total : 0;
     a.causal = causal != 0;
     // The kernels need c > 0: a zero scale is replaced by the smallest normal
     // float, for which every exp2 argument rounds to 0 exactly as with c = 0
@@ -221,6 +267,91 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
   const int st = validate(q, k, v, o, lse, batch, heads, n, d_k, scale, causal, dtype);
   if (st != FA_OK) return st;
   return run(q, k, v, o, lse, batch, heads, n, d_k, scale, causal, dtype, 1.0f, stream);
+}
+
+int fa_forward_strided(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                       int heads, int n, int d_k, const int64_t* strides, float scale, int causal,
+                       int dtype, void* stream) {
+  if (!q || !k || !v || !o || !strides) return FA_ERR_NULL;
+  if (batch < 1 || heads < 1 || n < 1) return FA_ERR_SHAPE;
+  if (dtype < FA_F32 || dtype > FA_FP8_E4M3) return FA_ERR_DTYPE;
+  if ((d_k != 64 && d_k != 128) || (causal != 0 && causal != 1)) return FA_ERR_UNSUPPORTED;
+  for (uintptr_t p : {(uintptr_t)q, (uintptr_t)k, (uintptr_t)v, (uintptr_t)o, (uintptr_t)lse})
+    if (p % 16) return FA_ERR_ALIGN;
+  if (!std::isfinite(scale) || scale < 0.f || !std::isfinite((float)(scale * kLog2e)))
+    return FA_ERR_SCALE;
+  const int ib = elt_bytes_in(dtype), ob = elt_bytes_out(dtype);
+  for (int i = 0; i < 12; ++i) {
+    const int eb = i < 9 ? ib : ob;
+    if (strides[i] < 0) return FA_ERR_UNSUPPORTED;
+    if ((strides[i] * eb) % 16) return FA_ERR_ALIGN;
+    if (strides[i] > (INT64_C(1) << 40)) return FA_ERR_OVERFLOW;
+  }
+  for (int t = 0; t < 4; ++t) {
+    const int64_t sr = strides[3 * t + 2];
+    const int eb = t < 3 ? ib : ob;
+    if (sr < d_k) return FA_ERR_UNSUPPORTED;  // rows of one head must not overlap
+    // one head's rows (plus the padding rows of the last tile) within the
+    // kernels' 32-bit buffer offsets
+    if (((int64_t)n + 256) * sr * eb > INT32_MAX) return FA_ERR_OVERFLOW;
+  }
+  const int64_t bh = (int64_t)batch * heads;
+  if (bh > kMaxGrid || bh * (((int64_t)n + 127) / 128) > kMaxGrid) return FA_ERR_OVERFLOW;
+  if (!rows_disjoint(strides + 9, batch, heads, n, d_k)) return FA_ERR_ALIAS;
+  const Range rq = strided_span(q, strides, batch, heads, n, d_k, ib);
+  const Range rk = strided_span(k, strides + 3, batch, heads, n, d_k, ib);
+  const Range rv = strided_span(v, strides + 6, batch, heads, n, d_k, ib);
+  const Range ro = strided_span(o, strides + 9, batch, heads, n, d_k, ob);
+  if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv)) return FA_ERR_ALIAS;
+  if (lse) {
+    const Range rl{(uintptr_t)lse, (uintptr_t)lse + (uintptr_t)(bh * n * 4)};
+    if (overlap(rl, rq) || overlap(rl, rk) || overlap(rl, rv) || overlap(rl, ro)) return FA_ERR_ALIAS;
+  }
+  Layout lay;
+  for (int i = 0; i < 12; ++i) lay.s[i] = strides[i];
+  lay.cu_seqlens = nullptr;
+  lay.total = 0;
+  return run(q, k, v, o, lse, batch, heads, n, d_k, scale, causal, dtype, 1.0f, stream, 1, nullptr,
+             &lay);
+}
+
+int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const int* cu_seqlens, int batch, int total, int max_seqlen, int heads,
+                      int d_k, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !cu_seqlens) return FA_ERR_NULL;
+  if (batch < 1 || heads < 1 || max_seqlen < 1 || total < 0) return FA_ERR_SHAPE;
+  if (dtype < FA_F32 || dtype > FA_FP8_E4M3) return FA_ERR_DTYPE;
+  if ((d_k != 64 && d_k != 128) || (causal != 0 && causal != 1)) return FA_ERR_UNSUPPORTED;
+  for (uintptr_t p : {(uintptr_t)q, (uintptr_t)k, (uintptr_t)v, (uintptr_t)o, (uintptr_t)lse})
+    if (p % 16) return FA_ERR_ALIGN;
+  if ((uintptr_t)cu_seqlens % 4) return FA_ERR_ALIGN;
+  if (!std::isfinite(scale) || scale < 0.f || !std::isfinite((float)(scale * kLog2e)))
+    return FA_ERR_SCALE;
+  const int ib = elt_bytes_in(dtype), ob = elt_bytes_out(dtype);
+  const int64_t rs = (int64_t)heads * d_k;  // row stride, elements
+  if (((int64_t)max_seqlen + 256) * rs * std::max(ib, ob) > INT32_MAX) return FA_ERR_OVERFLOW;
+  const int64_t bh = (int64_t)batch * heads;
+  if (bh > kMaxGrid || bh * (((int64_t)max_seqlen + 127) / 128) > kMaxGrid) return FA_ERR_OVERFLOW;
+  if ((int64_t)total * rs > (INT64_C(1) << 50)) return FA_ERR_OVERFLOW;
+  const Range rq{(uintptr_t)q, (uintptr_t)q + (uintptr_t)(total * rs * ib)};
+  const Range rk{(uintptr_t)k, (uintptr_t)k + (uintptr_t)(total * rs * ib)};
+  const Range rv{(uintptr_t)v, (uintptr_t)v + (uintptr_t)(total * rs * ib)};
+  const Range ro{(uintptr_t)o, (uintptr_t)o + (uintptr_t)(total * rs * ob)};
+  const Range rc{(uintptr_t)cu_seqlens, (uintptr_t)cu_seqlens + (uintptr_t)(batch + 1) * 4};
+  if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(ro, rc)) return FA_ERR_ALIAS;
+  if (lse) {
+    const Range rl{(uintptr_t)lse, (uintptr_t)lse + (uintptr_t)((int64_t)heads * total * 4)};
+    if (overlap(rl, rq) || overlap(rl, rk) || overlap(rl, rv) || overlap(rl, ro) || overlap(rl, rc))
+      return FA_ERR_ALIAS;
+  }
+  if (total == 0) return FA_OK;  // no rows: nothing to compute
+  Layout lay;
+  const int64_t s[3] = {0, d_k, rs};
+  for (int i = 0; i < 12; ++i) lay.s[i] = s[i % 3];
+  lay.cu_seqlens = cu_seqlens;
+  lay.total = total;
+  return run(q, k, v, o, lse, batch, heads, max_seqlen, d_k, scale, causal, dtype, 1.0f, stream, 1,
+             nullptr, &lay);
 }
 
 int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int batch,

@@ -32,13 +32,15 @@ struct TileId {
 // visited from the last one (the longest under a causal mask when a tile
 // holds query rows). When the number of (batch, head) pairs is a multiple of
 // 8, the workgroups of each head go to one XCD (workgroups are dispatched
-// round-robin over the 8 XCDs), so a head's tiles share that XCD's L2.
+// round-robin over the 8 XCDs), so a head's tiles share that XCD's L2; XCD x
+// holds the pairs x, x + 8, x + 16, ..., so consecutive heads -- the heads of
+// one sequence of a ragged batch -- spread over all XCDs.
 __device__ inline TileId tile_of_block(int pid, int bh_count, int tiles, bool reverse) {
   int bh, tt;
   if ((bh_count & 7) == 0) {
     const int xcd = pid & 7, slot = pid >> 3, per = bh_count >> 3;
     tt = slot / per;
-    bh = xcd * per + slot % per;
+    bh = (slot % per) * 8 + xcd;
   } else {
     tt = pid / bh_count;
     bh = pid % bh_count;

@@ -57,9 +57,9 @@ struct KeyTiles {
   int lo, hi;
 };
 template <int BK>
-__device__ inline KeyTiles key_tiles(const FwdArgs& a, int q_end, bool causal) {
+__device__ inline KeyTiles key_tiles(const FwdArgs& a, int n, int q_end, bool causal) {
   const int kbeg = blockIdx.y * a.split_keys;
-  int kend = min(a.n, kbeg + a.split_keys);
+  int kend = min(n, kbeg + a.split_keys);
   if (causal) kend = min(kend, q_end);
   const int lo = kbeg / BK;
   return {lo, kend > kbeg ? (kend + BK - 1) / BK : lo};
@@ -69,6 +69,53 @@ __device__ inline KeyTiles key_tiles(const FwdArgs& a, int q_end, bool causal) {
 // visible key yet (possible in a later key block) keeps -inf as its max but
 // exponentiates against 0, so its weights are exactly 0 rather than NaN.
 __device__ inline float exp_ref(float m) { return m == -INFINITY ? 0.f : m; }
+
+// One (batch, head) -- or one sequence of a ragged batch -- of the layout
+// described by FwdArgs: row 0 of q, k, v, o, the row strides in bytes (O's
+// in elements), the row count and the LSE of row 0. Ragged-batch offsets are
+// clamped to [0, total] and the length to n, so that no access leaves the
+// packed arrays whatever cu_seqlens holds.
+struct HeadView {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  uint8_t* o;
+  uint32_t qrs, krs, vrs;
+  size_t ors;
+  int n;
+  float* lse;
+};
+template <int IN_B, int OUT_B>
+__device__ inline HeadView head_view(const FwdArgs& a, int bh) {
+  const int b = bh / a.heads, h = bh - b * a.heads;
+  int64_t start = 0;
+  int n = a.n;
+  int64_t bq = b, bk = b, bv = b, bo = b;
+  if (a.cu_seqlens) {
+    const int s0 = min(max(a.cu_seqlens[b], 0), a.total);
+    const int s1 = min(max(a.cu_seqlens[b + 1], s0), a.total);
+    start = s0;
+    n = min(s1 - s0, a.n);
+    bq = bk = bv = bo = 0;
+  }
+  HeadView v;
+  v.q = (const uint8_t*)a.q + (bq * a.q_sb + h * a.q_sh + start * a.q_sr) * IN_B;
+  v.k = (const uint8_t*)a.k + (bk * a.k_sb + h * a.k_sh + start * a.k_sr) * IN_B;
+  v.v = (const uint8_t*)a.v + (bv * a.v_sb + h * a.v_sh + start * a.v_sr) * IN_B;
+  v.o = (uint8_t*)a.o + (bo * a.o_sb + h * a.o_sh + start * a.o_sr) * OUT_B;
+  v.qrs = (uint32_t)(a.q_sr * IN_B);
+  v.krs = (uint32_t)(a.k_sr * IN_B);
+  v.vrs = (uint32_t)(a.v_sr * IN_B);
+  v.ors = (size_t)a.o_sr;
+  v.n = n;
+  v.lse = !a.lse ? nullptr : a.cu_seqlens ? a.lse + (size_t)h * a.total + start : a.lse + (size_t)bh * a.n;
+  return v;
+}
+// Bytes a buffer resource must cover for `rows` rows of `row_bytes` at a
+// stride of `rs` bytes (0 rows: nothing).
+__device__ inline uint32_t span_bytes(int rows, uint32_t rs, int row_bytes) {
+  return rows > 0 ? (uint32_t)(rows - 1) * rs + (uint32_t)row_bytes : 0u;
+}
 
 // Split-KV partial result of one row (lane halves hold d-columns as in the
 // O^T accumulator): O_g = o / l (times o_mult), LSE_g; zeros and -inf when
@@ -163,25 +210,25 @@ void fwd_mfma16(FwdArgs a) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, provably uniform
   const int lane = tid & 63, lr = lane & 31, hl = lane >> 5;
-  const int n = a.n;
-  const int tiles = (n + kBq - 1) / kBq;
+  const int tiles = (a.n + kBq - 1) / kBq;
   const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
+  const HeadView hv = head_view<GB, 2>(a, tl.bh);
+  const int n = hv.n;
   const int q0 = tl.t * kBq;
+  if (q0 >= n) return;                // a tile past a short sequence (uniform)
   const int qw0 = q0 + 32 * w;        // first query row of this wave
   const int qrow = qw0 + lr;          // query row of this lane
-  const size_t head_off = (size_t)tl.bh * (size_t)n * D;
-  const uint32_t head_bytes = (uint32_t)n * D * GB;
 
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint8_t*)a.q + head_off * GB, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint8_t*)a.k + head_off * GB, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint8_t*)a.v + head_off * GB, head_bytes);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(hv.q, span_bytes(n, hv.qrs, D * GB));
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(hv.k, span_bytes(n, hv.krs, D * GB));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(hv.v, span_bytes(n, hv.vrs, D * GB));
 
   // Q fragments (B operand of S^T = K Q^T): lane holds query qrow, d-columns
   // ks*16 + hl*8 .. +8 for each k-step ks. Rows past n load as zeros.
   u32x4_t qf[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    const uint32_t off = ((uint32_t)qrow * D + ks * 16 + hl * 8) * GB;
+    const uint32_t off = (uint32_t)qrow * hv.qrs + (ks * 16 + hl * 8) * GB;
     if constexpr (F8) {
       const u32x2_t b = bload8(rq, off);
       qf[ks] = u32x4_t{e4m3x2_to_bf16x2<false>(b[0]), e4m3x2_to_bf16x2<true>(b[0]),
@@ -191,7 +238,7 @@ void fwd_mfma16(FwdArgs a) {
     }
   }
 
-  const KeyTiles kt = key_tiles<BK>(a, min(q0 + kBq, n), CAUSAL);
+  const KeyTiles kt = key_tiles<BK>(a, n, min(q0 + kBq, n), CAUSAL);
   const int j_lo = kt.lo, nt = kt.hi;  // key tiles j_lo .. nt-1
 
   // ---- staging of global tiles through registers
@@ -203,14 +250,14 @@ void fwd_mfma16(FwdArgs a) {
     for (int it = 0; it < NLD; ++it) {
       const int idx = tid + it * kThreads;
       const int row = idx / CPR, c = idx % CPR;
-      kst[it] = bload16(rk, ((uint32_t)(j * BK + row) * CPR + c) * 16);
+      kst[it] = bload16(rk, (uint32_t)(j * BK + row) * hv.krs + c * 16);
     }
   };
   auto load_v = [&](int j) {
 #pragma unroll
     for (int r = 0; r < NLD; ++r) {
       const int key = j * BK + NLD * vgrp + r;
-      vst[r] = bload16(rv, ((uint32_t)key * CPR + vch) * 16);
+      vst[r] = bload16(rv, (uint32_t)key * hv.vrs + vch * 16);
     }
   };
   auto store_k = [&](int slot) {
@@ -400,7 +447,7 @@ void fwd_mfma16(FwdArgs a) {
     store_partial<NDB>(a, tl.bh, qrow, hl, o, m2, lt);
   } else if (qrow < n) {
     const float inv = a.o_mult / lt;
-    uint16_t* Og = (uint16_t*)a.o + head_off + (size_t)qrow * D;
+    uint16_t* Og = (uint16_t*)hv.o + (size_t)qrow * hv.ors;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -411,7 +458,7 @@ void fwd_mfma16(FwdArgs a) {
         *(u32x2_t*)(Og + d) = u32x2_t{x0, x1};
       }
     }
-    if (hl == 0 && a.lse) a.lse[(size_t)tl.bh * n + qrow] = (m2 + __log2f(lt)) * kLn2;
+    if (hl == 0 && hv.lse) hv.lse[qrow] = (m2 + __log2f(lt)) * kLn2;
   }
 }
 // ---------------------------------------------------------------------------
@@ -485,19 +532,19 @@ void fwd_direct(FwdArgs a) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, provably uniform
   const int lane = tid & 63, lr = lane & 31, hl = lane >> 5;
-  const int n = a.n;
-  const int tiles = (n + kDirectBq - 1) / kDirectBq;
+  const int tiles = (a.n + kDirectBq - 1) / kDirectBq;
   const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
+  const HeadView hv = head_view<2, 2>(a, tl.bh);
+  const int n = hv.n;
   const int q0 = tl.t * kDirectBq;
+  if (q0 >= n) return;  // a tile past a short sequence (uniform)
   const int qw0 = q0 + 32 * w;
   const int qrow = qw0 + lr;
-  const size_t head_off = (size_t)tl.bh * (size_t)n * D;
-  const uint32_t head_bytes = (uint32_t)n * ROWB;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint8_t*)a.q + head_off * 2, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint8_t*)a.k + head_off * 2, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint8_t*)a.v + head_off * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(hv.q, span_bytes(n, hv.qrs, ROWB));
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(hv.k, span_bytes(n, hv.krs, ROWB));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(hv.v, span_bytes(n, hv.vrs, ROWB));
 
-  const KeyTiles kt = key_tiles<BK>(a, min(q0 + kDirectBq, n), CAUSAL);
+  const KeyTiles kt = key_tiles<BK>(a, n, min(q0 + kDirectBq, n), CAUSAL);
   const int j_lo = kt.lo, nt = kt.hi;  // key tiles j_lo .. nt-1 (ring slots relative to j_lo)
 
   // Per-lane source offsets of this wave's share of a tile (tile 0).
@@ -506,8 +553,8 @@ void fwd_direct(FwdArgs a) {
   for (int i = 0; i < LPW; ++i) {
     const int byte = (w * LPW + i) * 1024 + lane * 16;
     const int row = byte / ROWB, p = (byte % ROWB) / 16;
-    koff[i] = (uint32_t)(row * ROWB + (p ^ L::kswz(row)) * 16);
-    voff[i] = (uint32_t)(row * ROWB + (p ^ L::vswz(row)) * 16);
+    koff[i] = (uint32_t)row * hv.krs + (uint32_t)((p ^ L::kswz(row)) * 16);
+    voff[i] = (uint32_t)row * hv.vrs + (uint32_t)((p ^ L::vswz(row)) * 16);
   }
   // Issue the loads of tile t into a slot; tiles past the loop load nothing
   // (an offset past the buffer end returns zeros without a memory access),
@@ -515,11 +562,12 @@ void fwd_direct(FwdArgs a) {
   // through inline assembly: the compiler does not track them, and the
   // explicit vmcnt wait plus barrier in each step orders them.
   auto issue = [&](LdsSlot<TILE_B>& slot, int t) __attribute__((always_inline)) {
-    const uint32_t base = t < nt ? (uint32_t)t * TILE_B : 0x80000000u;
+    const uint32_t kb = t < nt ? (uint32_t)(t * BK) * hv.krs : 0x80000000u;
+    const uint32_t vb = t < nt ? (uint32_t)(t * BK) * hv.vrs : 0x80000000u;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      lds_dma16(rk, slot.k + (w * LPW + i) * 1024, base + koff[i]);
-      lds_dma16(rv, slot.v + (w * LPW + i) * 1024, base + voff[i]);
+      lds_dma16(rk, slot.k + (w * LPW + i) * 1024, kb + koff[i]);
+      lds_dma16(rv, slot.v + (w * LPW + i) * 1024, vb + voff[i]);
     }
   };
 
@@ -527,7 +575,7 @@ void fwd_direct(FwdArgs a) {
   u32x4_t qf[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
-    qf[ks] = bload16(rq, ((uint32_t)qrow * D + ks * 16 + hl * 8) * 2);
+    qf[ks] = bload16(rq, (uint32_t)qrow * hv.qrs + (ks * 16 + hl * 8) * 2);
   wait_vmcnt<0>();
 
   // Per-lane LDS read offsets.
@@ -673,7 +721,7 @@ void fwd_direct(FwdArgs a) {
     store_partial<NDB>(a, tl.bh, qrow, hl, o, m2, lt);
   } else if (qrow < n) {
     const float inv = a.o_mult / lt;
-    uint16_t* Og = (uint16_t*)a.o + head_off + (size_t)qrow * D;
+    uint16_t* Og = (uint16_t*)hv.o + (size_t)qrow * hv.ors;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -684,7 +732,7 @@ void fwd_direct(FwdArgs a) {
         *(u32x2_t*)(Og + d) = u32x2_t{x0, x1};
       }
     }
-    if (hl == 0 && a.lse) a.lse[(size_t)tl.bh * n + qrow] = (m2 + __log2f(lt)) * kLn2;
+    if (hl == 0 && hv.lse) hv.lse[qrow] = (m2 + __log2f(lt)) * kLn2;
   }
 }
 
@@ -712,21 +760,23 @@ void fwd_mfma32(FwdArgs a) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, provably uniform
   const int lane = tid & 63, lr = lane & 31, hl = lane >> 5;
-  const int n = a.n;
-  const int tiles = (n + kBq - 1) / kBq;
+  const int tiles = (a.n + kBq - 1) / kBq;
   const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
+  const HeadView hv = head_view<4, 4>(a, tl.bh);
+  const int n = hv.n;
   const int q0 = tl.t * kBq;
+  if (q0 >= n) return;  // a tile past a short sequence (uniform)
   const int qw0 = q0 + 32 * w;
   const int qrow = qw0 + lr;
-  const size_t head_off = (size_t)tl.bh * (size_t)n * D;
-  const float* Qg = (const float*)a.q + head_off;
-  const u32x4_t* Kg = (const u32x4_t*)((const float*)a.k + head_off);
-  const u32x4_t* Vg = (const u32x4_t*)((const float*)a.v + head_off);
+  // row r of q, k, v (16-byte chunks of a row are contiguous)
+  auto qrow_ptr = [&](int r) { return (const u32x4_t*)(hv.q + (size_t)r * hv.qrs); };
+  auto krow_ptr = [&](int r) { return (const u32x4_t*)(hv.k + (size_t)r * hv.krs); };
+  auto vrow_ptr = [&](int r) { return (const u32x4_t*)(hv.v + (size_t)r * hv.vrs); };
 
   float qf[HALF];
   {
     const bool ok = qrow < n;
-    const u32x4_t* qp = (const u32x4_t*)(Qg + (size_t)(ok ? qrow : 0) * D + hl * HALF);
+    const u32x4_t* qp = qrow_ptr(ok ? qrow : 0) + hl * HALF / 4;
 #pragma unroll
     for (int i = 0; i < HALF / 4; ++i) {
       u32x4_t x = qp[i];
@@ -735,7 +785,7 @@ void fwd_mfma32(FwdArgs a) {
     }
   }
 
-  const KeyTiles kt = key_tiles<BK>(a, min(q0 + kBq, n), CAUSAL);
+  const KeyTiles kt = key_tiles<BK>(a, n, min(q0 + kBq, n), CAUSAL);
   const int j_lo = kt.lo, nt = kt.hi;  // key tiles j_lo .. nt-1
 
   u32x4_t kreg[NLD], vreg[NLD];
@@ -747,8 +797,8 @@ void fwd_mfma32(FwdArgs a) {
       const int row = idx / CPR, ch = idx % CPR;
       const int key = key0 + row;
       const bool ok = key < n;
-      kreg[it] = ok ? Kg[(size_t)key * CPR + ch] : u32x4_t{0, 0, 0, 0};
-      vreg[it] = ok ? Vg[(size_t)key * CPR + ch] : u32x4_t{0, 0, 0, 0};
+      kreg[it] = ok ? krow_ptr(key)[ch] : u32x4_t{0, 0, 0, 0};
+      vreg[it] = ok ? vrow_ptr(key)[ch] : u32x4_t{0, 0, 0, 0};
     }
   };
   auto swrite = [&](int buf) {
@@ -837,7 +887,7 @@ void fwd_mfma32(FwdArgs a) {
     store_partial<NDB>(a, tl.bh, qrow, hl, o, m2, lt);
   } else if (qrow < n) {
     const float inv = a.o_mult / lt;
-    float* Og = (float*)a.o + head_off + (size_t)qrow * D;
+    float* Og = (float*)hv.o + (size_t)qrow * hv.ors;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -849,7 +899,7 @@ void fwd_mfma32(FwdArgs a) {
         *(u32x4_t*)(Og + d) = x;
       }
     }
-    if (hl == 0 && a.lse) a.lse[(size_t)tl.bh * n + qrow] = (m2 + __log2f(lt)) * kLn2;
+    if (hl == 0 && hv.lse) hv.lse[qrow] = (m2 + __log2f(lt)) * kLn2;
   }
 }
 

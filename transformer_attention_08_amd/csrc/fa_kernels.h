@@ -18,8 +18,18 @@ struct FwdArgs {
   void* o;
   float* lse;      // may be null
   int bh;          // batch * heads
-  int n;           // queries = keys per (batch, head)
+  int n;           // queries = keys per (batch, head); the longest sequence with cu_seqlens
   int d;           // 64 or 128
+  // Layout, in elements: element (b, h, i, c) of q is q[b*q_sb + h*q_sh + i*q_sr + c];
+  // likewise k, v, o. The dense [batch, heads, n, d] layout has
+  // (sb, sh, sr) = (heads*n*d, n*d, d). LSE is [bh][n] (dense rows).
+  int heads;
+  int64_t q_sb, q_sh, q_sr, k_sb, k_sh, k_sr, v_sb, v_sh, v_sr, o_sb, o_sh, o_sr;
+  // Ragged batches: when set, sequence b is rows cu_seqlens[b] .. cu_seqlens[b+1]
+  // of a packed row axis of `total` rows (the batch strides are then unused)
+  // and LSE is [heads][total].
+  const int* cu_seqlens;
+  int total;
   bool causal;
   float c;         // scale (times both fp8 descales) times log2(e)
   float o_mult;    // multiplier applied to O in the epilogue (v descale; 1 otherwise)
