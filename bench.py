@@ -110,6 +110,35 @@ def cpu_baseline(w, inp, budget_s: float = 15.0):
                       f"{elapsed:.1f} s"}
 
 
+def cpu_baseline_backward(w, inp, do, budget_s: float = 15.0):
+    """The fp64 gradient oracle on whole heads of the same inputs (S, P, dP, dS
+    materialised), as many heads as fit the time budget (at least one);
+    TFLOP/s under the backward FLOP count."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    qb, kb, vb = inp.bits("q"), inp.bits("k"), inp.bits("v")
+    gb = do.contiguous().view(__import__("torch").int16).numpy().view("uint16")
+    done, elapsed = 0, 0.0
+    while done < w.heads * w.batch:
+        bi, hi = divmod(done, w.heads)
+        q, k, v, g = (oracle.decode(x[bi:bi + 1, hi:hi + 1], w.dtype) for x in (qb, kb, vb, gb))
+        t0 = time.perf_counter()
+        oracle.attention_backward(q, k, v, g, w.scale, w.causal)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        if elapsed >= budget_s or elapsed / done * (done + 1) > 2 * budget_s:
+            break
+    fl = 10.0 * done * w.n * w.n * w.d_k / (2 if w.causal else 1)
+    return {"value": fl / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {w.batch * w.heads} heads, all {w.n} rows each, fp64 NumPy "
+                      f"(S, P, dP, dS materialised), {elapsed:.1f} s"}
+
+
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     """A plain device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
     import torch
@@ -196,6 +225,8 @@ def bench_backward(args, w):
                      "frac": round(tflops / peak, 4), "traffic": None,
                      "kernel": "bwd_dq+bwd_dkdv"},
     }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_backward(w, inp, do)
     print(json.dumps(line), flush=True)
     return 0
 

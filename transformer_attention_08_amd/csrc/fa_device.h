@@ -34,13 +34,20 @@ struct TileId {
 // 8, the workgroups of each head go to one XCD (workgroups are dispatched
 // round-robin over the 8 XCDs), so a head's tiles share that XCD's L2; XCD x
 // holds the pairs x, x + 8, x + 16, ..., so consecutive heads -- the heads of
-// one sequence of a ragged batch -- spread over all XCDs.
+// one sequence of a ragged batch -- spread over all XCDs. Each XCD takes its
+// heads in groups of G, the longest tiles of a group first: a head's
+// workgroups then run close together and re-read its K/V tiles from L2
+// rather than HBM. Long heads (32 tiles or more) use groups of 2; short ones
+// one group, where the longest tiles of every head going first matters more
+// for the tail than the re-reads.
 __device__ inline TileId tile_of_block(int pid, int bh_count, int tiles, bool reverse) {
   int bh, tt;
   if ((bh_count & 7) == 0) {
     const int xcd = pid & 7, slot = pid >> 3, per = bh_count >> 3;
-    tt = slot / per;
-    bh = (slot % per) * 8 + xcd;
+    const int G = (tiles >= 32 && (per & 1) == 0) ? 2 : per;
+    const int g = slot / (G * tiles), r = slot - g * (G * tiles);
+    tt = r / G;
+    bh = (g * G + r % G) * 8 + xcd;
   } else {
     tt = pid / bh_count;
     bh = pid % bh_count;
