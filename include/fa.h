@@ -167,8 +167,8 @@ int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, floa
  * rounding.
  *
  *   splits      requested number of key blocks, 1 .. 256. Block g holds
- *               keys [g*B, min(n, (g+1)*B)) with B = 64 * ceil(ceil(n /
- *               splits) / 64), so ceil(n / B) blocks are used (one block:
+ *               keys [g*B, min(n, (g+1)*B)) with B = 128 * ceil(ceil(n /
+ *               splits) / 128), so ceil(n / B) blocks are used (one block:
  *               plain fa_forward, no workspace). The workspace holds fp32
  *               O_g [blocks][batch][heads][n][d_k] from byte 0 and fp32
  *               LSE_g [blocks][batch][heads][n] from the next multiple of

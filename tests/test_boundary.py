@@ -102,7 +102,7 @@ def test_valid_call_without_gpu_reports_hip_error(lib):
 def block_keys(n, splits):
     """Keys per split-KV block, the rule stated in include/fa.h."""
     per = -(-n // splits)
-    return 64 * -(-per // 64)
+    return 128 * -(-per // 128)
 
 
 @pytest.mark.parametrize("n,splits", [(1, 1), (100, 1), (100, 2), (64, 2), (65, 2), (8192, 7),

@@ -28,7 +28,7 @@ def say(*a):
 
 def block_keys(n, splits):
     per = -(-n // splits)
-    return 64 * -(-per // 64)
+    return 128 * -(-per // 128)
 
 
 def make(b, h, n, d, dtype, seed):
@@ -50,7 +50,7 @@ def run_split(inp, splits, causal, scale):
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "fp8"])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("n,splits", [(65, 2), (300, 3), (1000, 7), (2048, 64), (130, 256)])
+@pytest.mark.parametrize("n,splits", [(201, 2), (300, 3), (1000, 7), (2048, 64), (130, 256)])
 def test_merged_result_matches_oracle(n, splits, causal, dtype):
     b, h, d = 1, 3, (64 if n % 2 else 128)
     say(f"splitkv n={n} splits={splits} causal={causal} dtype={dtype} d={d}")
@@ -120,7 +120,7 @@ def test_one_block_is_the_plain_forward_bitwise():
     d = inp.to("cuda")
     o1, l1 = fa.forward(d.q, d.k, d.v, causal=True)
     o2, l2, _ = fa.forward_splitkv(d.q, d.k, d.v, 1, causal=True)
-    o3, l3, _ = fa.forward_splitkv(d.q, d.k, d.v, 64, causal=True)   # 500 keys -> 64-key blocks
+    o3, l3, _ = fa.forward_splitkv(d.q, d.k, d.v, 64, causal=True)   # 500 keys -> 128-key blocks
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.isfinite(o3).all()

@@ -65,12 +65,12 @@ int validate(const void* q, const void* k, const void* v, void* o, const float* 
 }
 
 // Keys per split-KV block for a requested number of blocks (a multiple of
-// 64, the coarsest key tile of the kernels), and the number of blocks that
-// results.
+// 128, the coarsest key tile of the kernels, so that every block starts on a
+// tile boundary), and the number of blocks that results.
 constexpr int kMaxSplits = 256;
 int split_keys_for(int n, int splits) {
   const int64_t per = ((int64_t)n + splits - 1) / splits;
-  return (int)(((per + 63) / 64) * 64);
+  return (int)(((per + 127) / 128) * 128);
 }
 int splits_used(int n, int splits) {
   const int sk = split_keys_for(n, splits);

@@ -463,10 +463,11 @@ void fwd_mfma16(FwdArgs a) {
 }
 // ---------------------------------------------------------------------------
 // Direct-to-LDS kernel for f16 / bf16 inputs. Eight waves (256 query rows)
-// per workgroup, 64-key tiles, and an NS-stage ring of K/V tiles in LDS that
-// the buffer unit fills directly (buffer_load ... lds): no staging registers,
-// no VALU work to move tiles, and NS - 1 tiles of prefetch to hide memory
-// latency. Loads past the end of a head return zeros.
+// per workgroup, 128-key tiles, and an NS-stage ring (2 stages: 128 KiB of
+// LDS at d_k 128) of K/V tiles in LDS that the buffer unit fills directly
+// (buffer_load ... lds): no staging registers, no VALU work to move tiles,
+// and NS - 1 tiles of prefetch to hide memory latency. Loads past the end of
+// a head return zeros.
 //
 // LDS layouts. K rows are stored as they are in memory but with their
 // 16-byte chunks XOR-swizzled by row, so that the 16 rows one MFMA operand
@@ -487,13 +488,13 @@ void fwd_mfma16(FwdArgs a) {
 #define FA_DIRECT_WAVES 8
 #endif
 #ifndef FA_DIRECT_KEYS
-#define FA_DIRECT_KEYS 64
+#define FA_DIRECT_KEYS 128
 #endif
 constexpr int kDirectWaves = FA_DIRECT_WAVES;
 constexpr int kDirectThreads = 64 * kDirectWaves;
 constexpr int kDirectBq = 32 * kDirectWaves;
 #ifndef FA_STAGES
-#define FA_STAGES 4
+#define FA_STAGES 2
 #endif
 
 template <int D>

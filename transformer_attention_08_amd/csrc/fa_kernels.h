@@ -34,7 +34,7 @@ struct FwdArgs {
   float c;         // scale (times both fp8 descales) times log2(e)
   float o_mult;    // multiplier applied to O in the epilogue (v descale; 1 otherwise)
   Elt elt;
-  // Split-KV: the keys are cut into blocks of split_keys (a multiple of 64;
+  // Split-KV: the keys are cut into blocks of split_keys (a multiple of 128;
   // n when the keys are not split) and grid dimension y runs over the blocks.
   // When part_o is set, each block writes its partial result there instead of
   // o / lse: O_g normalised by its own row sum, fp32 [splits][bh][n][d], and
