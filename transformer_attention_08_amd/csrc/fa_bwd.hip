@@ -41,7 +41,16 @@
 namespace fa {
 namespace {
 
-constexpr int kBwdStages = 4;
+// Ring stages and tile rows (keys in pass 1, queries in pass 2) of the
+// backward kernels.
+#ifndef FA_BWD_STAGES
+#define FA_BWD_STAGES 4
+#endif
+#ifndef FA_BWD_TILE
+#define FA_BWD_TILE 64
+#endif
+constexpr int kBwdStages = FA_BWD_STAGES;
+static_assert(kBwdStages >= 2 && kBwdStages <= 4, "stages");
 
 // Chunk swizzle for rows of D 16-bit elements: bijective on the 16 rows of
 // one row-wise read, and distinct in its upper bits (D = 128: bits 2-3 over
@@ -113,7 +122,7 @@ struct PairSlot {
 template <Elt IN, int D, bool CAUSAL>
 __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq(BwdArgs a) {
-  constexpr int ROWB = D * 2, BK = 64, TILE_B = BK * ROWB;
+  constexpr int ROWB = D * 2, BK = FA_BWD_TILE, TILE_B = BK * ROWB;
   constexpr int LPW = TILE_B / 1024 / kDqWaves;  // 1 KiB loads per wave per tile (K and V each)
   constexpr int NS = kBwdStages;
   constexpr int KB = BK / 32, NKS = D / 16, NDB = D / 32;
@@ -260,13 +269,13 @@ void bwd_dq(BwdArgs a) {
   __syncthreads();
 
   issue(ring0, 0);
-  issue(ring1, 1);
-  issue(ring2, 2);
+  if constexpr (NS > 2) issue(ring1, 1);
+  if constexpr (NS > 3) issue(ring2, 2);
   for (int j0 = 0; j0 < nt; j0 += NS) {
     step(std::integral_constant<int, 0>{}, j0);
     if (j0 + 1 < nt) step(std::integral_constant<int, 1>{}, j0 + 1);
-    if (j0 + 2 < nt) step(std::integral_constant<int, 2>{}, j0 + 2);
-    if (j0 + 3 < nt) step(std::integral_constant<int, 3>{}, j0 + 3);
+    if constexpr (NS > 2) if (j0 + 2 < nt) step(std::integral_constant<int, 2>{}, j0 + 2);
+    if constexpr (NS > 3) if (j0 + 3 < nt) step(std::integral_constant<int, 3>{}, j0 + 3);
   }
   wait_vmcnt<0>();
 
@@ -284,7 +293,7 @@ void bwd_dq(BwdArgs a) {
 constexpr int kKvWaves = 4;
 constexpr int kKvThreads = 64 * kKvWaves;
 constexpr int kKvBk = 32 * kKvWaves;  // keys per workgroup
-constexpr int kKvBq = 64;             // queries per tile
+constexpr int kKvBq = FA_BWD_TILE;    // queries per tile
 
 template <int BYTES>
 struct QSlot {
@@ -470,13 +479,13 @@ void bwd_dkdv(BwdArgs a) {
   __syncthreads();
 
   issue(ring0, i_lo);
-  issue(ring1, i_lo + 1);
-  issue(ring2, i_lo + 2);
+  if constexpr (NS > 2) issue(ring1, i_lo + 1);
+  if constexpr (NS > 3) issue(ring2, i_lo + 2);
   for (int i0 = i_lo; i0 < nt; i0 += NS) {
     step(std::integral_constant<int, 0>{}, i0);
     if (i0 + 1 < nt) step(std::integral_constant<int, 1>{}, i0 + 1);
-    if (i0 + 2 < nt) step(std::integral_constant<int, 2>{}, i0 + 2);
-    if (i0 + 3 < nt) step(std::integral_constant<int, 3>{}, i0 + 3);
+    if constexpr (NS > 2) if (i0 + 2 < nt) step(std::integral_constant<int, 2>{}, i0 + 2);
+    if constexpr (NS > 3) if (i0 + 3 < nt) step(std::integral_constant<int, 3>{}, i0 + 3);
   }
   wait_vmcnt<0>();
 
