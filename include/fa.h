@@ -228,6 +228,24 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
 size_t fa_backward_workspace_size(int batch, int heads, int n);
 
 /*
+ * fa_backward_varlen -- fa_backward over a ragged batch, the gradients of
+ * fa_forward_varlen: q, k, v, o, dout, dq, dk, dv are [total, heads, d_k]
+ * packed rows, lse is [heads, total] (as fa_forward_varlen writes it), and
+ * cu_seqlens, batch, total and max_seqlen are as for fa_forward_varlen (the
+ * same clamping applies). Packed rows with equal lengths are also the
+ * [batch, n, heads, d_k] layout. The workspace must hold
+ * fa_backward_workspace_size(1, heads, total) bytes; on return it holds D and
+ * -LSE * log2(e) as [heads, total] fp32 arrays (the second from the next
+ * multiple of 256 bytes). total = 0 returns FA_OK without launching. Other
+ * arguments and errors as fa_backward.
+ */
+int fa_backward_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                       const float* lse, void* dq, void* dk, void* dv, const int* cu_seqlens,
+                       int batch, int total, int max_seqlen, int heads, int d_k, float scale,
+                       int causal, int dtype, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
  * fa_forward_unfused -- the same O and LSE as fa_forward (f16 / bf16), computed
  * step by step with S and P written to memory: S = scale Q K^T (causal
  * entries -inf) as fp32, then a row softmax writing P in the input type and

@@ -287,3 +287,25 @@ def test_varlen_validation(lib):
     assert vcall(lib, maxlen=1 << 20, h=32) == 8
     # no rows: valid and nothing is launched, so no HIP call is made
     assert vcall(lib, total=0) == 0
+
+
+def bvcall(lib, q=Q, k=K, v=V, o=OB, do=DO, lse=L, dq=DQ, dk=DK, dv=DV, cu=BASE + 31 * SPAN, batch=4,
+           total=1000, maxlen=600, h=2, d=128, scale=0.125, causal=1, dtype=2, ws=WS, wsb=1 << 20):
+    return lib.fa_backward_varlen(q, k, v, o, do, lse, dq, dk, dv, cu, batch, total, maxlen, h, d, scale,
+                                  causal, dtype, ws, wsb, None)
+
+
+def test_backward_varlen_validation(lib):
+    C = BASE + 31 * SPAN
+    assert bvcall(lib, cu=None) == 1 and bvcall(lib, ws=None) == 1 and bvcall(lib, do=None) == 1
+    assert bvcall(lib, batch=0) == 2 and bvcall(lib, maxlen=0) == 2 and bvcall(lib, total=-3) == 2
+    need = lib.fa_backward_workspace_size(1, 2, 1000)
+    assert bvcall(lib, wsb=need - 1) == 2
+    assert bvcall(lib, dtype=9) == 3 and bvcall(lib, dtype=0) == 4 and bvcall(lib, d=80) == 4
+    assert bvcall(lib, cu=C + 2) == 5 and bvcall(lib, dk=DK + 8) == 5
+    assert bvcall(lib, scale=float("nan")) == 6
+    assert bvcall(lib, dq=Q) == 7 and bvcall(lib, ws=C) == 7 and bvcall(lib, dv=DK + 64) == 7
+    assert bvcall(lib, maxlen=1 << 20, h=32) == 8
+    assert bvcall(lib, total=0) == 0   # no rows: returns before any HIP call
+    if torch.cuda.device_count() == 0:
+        assert bvcall(lib) == 9

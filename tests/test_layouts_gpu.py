@@ -154,3 +154,41 @@ def test_varlen_empty_sequences_around_one():
     o1, l1 = fa.forward(inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o1[0], o.transpose(0, 1)) and torch.equal(l1[0], lse)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_varlen_equals_per_sequence_calls(d, causal, dtype):
+    lens = [1, 17, 0, 300, 64, 129, 700, 2]
+    total, h = sum(lens), 3
+    say(f"backward varlen d={d} causal={causal} dtype={dtype} lens={lens}")
+    inp, do = workload.make_inputs_with_grad(1, h, total, d, dtype, seed=d + 7)
+    q, k, v, cu = pack(inp, lens)
+    g = do[0].transpose(0, 1).contiguous()
+    qd, kd, vd, gd, cud = (t.cuda() for t in (q, k, v, g, cu))
+    scale = float(np.float32(1 / math.sqrt(d)))
+    o, lse = fa.forward_varlen(qd, kd, vd, cud, max(lens), causal=causal, scale=scale)
+    dq, dk, dv = fa.backward_varlen(qd, kd, vd, o, lse, gd, cud, max(lens), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    for bi, ln in enumerate(lens):
+        if ln == 0:
+            continue
+        s0 = int(cu[bi])
+        sl = slice(s0, s0 + ln)
+        one = [t[sl].transpose(0, 1).unsqueeze(0).contiguous() for t in (qd, kd, vd, o, gd)]
+        l1 = lse[:, sl].unsqueeze(0).contiguous()
+        r = fa.backward(one[0], one[1], one[2], one[3], l1, one[4], causal=causal, scale=scale)
+        torch.cuda.synchronize()
+        for name, a_, b_ in zip(("dq", "dk", "dv"), r, (dq, dk, dv)):
+            assert torch.equal(a_[0], b_[sl].transpose(0, 1)), (bi, ln, name)
+    # the longest sequence against the gradient oracle (bar of test_backward_gpu)
+    s0, ln = int(cu[6]), lens[6]
+    sl = slice(s0, s0 + ln)
+    dec = lambda t: oracle.decode(t.cpu().contiguous().view(torch.int16).numpy().view("uint16"), dtype)
+    qs, ks, vs, gs = (dec(t[sl].transpose(0, 1).unsqueeze(0)) for t in (qd, kd, vd, gd))
+    ref = oracle.attention_backward(qs, ks, vs, gs, scale, causal)
+    tol = {"bf16": 1e-2, "f16": 2e-3}[dtype]
+    for name, gt, rf in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        got = dec(gt[sl].transpose(0, 1).unsqueeze(0))
+        assert np.abs(got - rf).max() <= tol * max(np.abs(rf).max(), 1e-3), name

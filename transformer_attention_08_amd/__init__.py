@@ -35,7 +35,7 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_DTYPE",
 
 EXPORTS = ("fa_forward", "fa_forward_fp8", "fa_forward_strided", "fa_forward_varlen",
            "fa_forward_splitkv", "fa_splitkv_workspace_size",
-           "fa_backward", "fa_backward_workspace_size", "fa_forward_unfused",
+           "fa_backward", "fa_backward_workspace_size", "fa_backward_varlen", "fa_forward_unfused",
            "fa_unfused_workspace_size", "fa_status_string", "fa_last_hip_error",
            "fa_abi_version")
 
@@ -71,6 +71,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_backward.restype = i
     lib.fa_backward_workspace_size.argtypes = [i, i, i]
     lib.fa_backward_workspace_size.restype = sz
+    lib.fa_backward_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i,
+                                       vp, sz, vp]
+    lib.fa_backward_varlen.restype = i
     lib.fa_forward_unfused.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp]
     lib.fa_forward_unfused.restype = i
     lib.fa_unfused_workspace_size.argtypes = [i, i, i]
@@ -332,3 +335,37 @@ def forward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens
                               _DTYPE_CODE[q.dtype], _stream(q.device))
     _check(r)
     return out, lse
+
+
+def backward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                    lse: torch.Tensor, dout: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+                    causal: bool = False, scale: Optional[float] = None,
+                    workspace: Optional[torch.Tensor] = None):
+    """``fa_backward_varlen``: (dQ, dK, dV) [total, heads, d_k] of ``forward_varlen``,
+    given its O [total, heads, d_k] and LSE [heads, total] and dO."""
+    lib = load_library()
+    if q.dtype not in (torch.float16, torch.bfloat16) or q.dim() != 3:
+        raise ValueError("backward_varlen takes [total, heads, d_k] float16 / bfloat16 tensors")
+    for t in (k, v, o, dout):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o and dout must share one shape and dtype")
+    for t in (q, k, v, o, dout, lse, cu_seqlens):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous device tensors")
+    total, h, d = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (h, total):
+        raise ValueError("lse must be float32 [heads, total]")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    if workspace is None:
+        workspace = torch.empty(max(backward_workspace_size(1, h, max(total, 1)), 16),
+                                dtype=torch.uint8, device=q.device)
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib.fa_backward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                _ptr(dk), _ptr(dv), _ptr(cu_seqlens), cu_seqlens.numel() - 1, total,
+                                int(max_seqlen), h, d, s, 1 if causal else 0, _DTYPE_CODE[q.dtype],
+                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(q.device))
+    _check(st)
+    return dq, dk, dv

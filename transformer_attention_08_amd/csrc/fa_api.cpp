@@ -122,7 +122,7 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
   const int64_t rows = bh * n;
   if (bh > kMaxGrid || bh * (((int64_t)n + 127) / 128) > kMaxGrid) return FA_ERR_OVERFLOW;
   if (rows > (INT64_C(1) << 62) / ((int64_t)d_k * 4)) return FA_ERR_OVERFLOW;
-  if ((int64_t)n * d_k * 2 > INT32_MAX) return FA_ERR_OVERFLOW;
+  if (((int64_t)n + 256) * d_k * 2 > INT32_MAX) return FA_ERR_OVERFLOW;
   const BwdLayout wl = bwd_layout(batch, heads, n);
   if (workspace_bytes < wl.total) return FA_ERR_SHAPE;
   const uintptr_t t_sz = (uintptr_t)(rows * d_k * 2);
@@ -250,6 +250,50 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int ba
       cb.out = dtype == FA_F32 ? fa::Elt::F32 : dtype == FA_F16 ? fa::Elt::F16 : fa::Elt::BF16;
       e = fa::launch_combine(cb, static_cast<hipStream_t>(stream));
     }
+  }
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+// Launch the two backward kernels for validated arguments. Dense layout when
+// cu_seqlens is null; otherwise packed [total, heads, d_k] rows.
+int run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+            const float* lse, void* dq, void* dk, void* dv, int batch, int heads, int n, int d_k,
+            float scale, int causal, int dtype, void* workspace, const int* cu_seqlens, int total,
+            void* stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) {
+    const BwdLayout wl = cu_seqlens ? bwd_layout(1, heads, total) : bwd_layout(batch, heads, n);
+    fa::BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.lse = lse;
+    a.delta = (float*)workspace;
+    a.nlse2 = (float*)((char*)workspace + wl.nl_off);
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.bh = batch * heads;
+    a.n = n;
+    a.d = d_k;
+    a.heads = heads;
+    a.rs = cu_seqlens ? (int64_t)heads * d_k : d_k;
+    a.cu_seqlens = cu_seqlens;
+    a.total = total;
+    a.causal = causal != 0;
+    float c = (float)(scale * kLog2e);
+    if (!(c > 0.f)) c = FLT_MIN;  // as in the forward: a zero scale gives uniform weights
+    a.c = c;
+    a.scale = scale;
+    a.elt = static_cast<fa::Elt>(dtype);
+    e = fa::launch_backward(a, static_cast<hipStream_t>(stream));
   }
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
@@ -467,38 +511,55 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
   const int st = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, batch, heads, n, d_k, scale,
                               causal, dtype, workspace, workspace_bytes);
   if (st != FA_OK) return st;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) {
-    const BwdLayout wl = bwd_layout(batch, heads, n);
-    fa::BwdArgs a;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.o = o;
-    a.dout = dout;
-    a.lse = lse;
-    a.delta = (float*)workspace;
-    a.nlse2 = (float*)((char*)workspace + wl.nl_off);
-    a.dq = dq;
-    a.dk = dk;
-    a.dv = dv;
-    a.bh = batch * heads;
-    a.n = n;
-    a.d = d_k;
-    a.causal = causal != 0;
-    float c = (float)(scale * kLog2e);
-    if (!(c > 0.f)) c = FLT_MIN;  // as in the forward: a zero scale gives uniform weights
-    a.c = c;
-    a.scale = scale;
-    a.elt = static_cast<fa::Elt>(dtype);
-    e = fa::launch_backward(a, static_cast<hipStream_t>(stream));
+  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, batch, heads, n, d_k, scale, causal, dtype,
+                 workspace, nullptr, 0, stream);
+}
+
+int fa_backward_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                       const float* lse, void* dq, void* dk, void* dv, const int* cu_seqlens,
+                       int batch, int total, int max_seqlen, int heads, int d_k, float scale,
+                       int causal, int dtype, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace || !cu_seqlens)
+    return FA_ERR_NULL;
+  if (batch < 1 || heads < 1 || max_seqlen < 1 || total < 0) return FA_ERR_SHAPE;
+  if (dtype < FA_F32 || dtype > FA_FP8_E4M3) return FA_ERR_DTYPE;
+  if ((dtype != FA_F16 && dtype != FA_BF16) || (d_k != 64 && d_k != 128) ||
+      (causal != 0 && causal != 1))
+    return FA_ERR_UNSUPPORTED;
+  for (uintptr_t p : {(uintptr_t)q, (uintptr_t)k, (uintptr_t)v, (uintptr_t)o, (uintptr_t)dout,
+                      (uintptr_t)lse, (uintptr_t)dq, (uintptr_t)dk, (uintptr_t)dv,
+                      (uintptr_t)workspace})
+    if (p % 16) return FA_ERR_ALIGN;
+  if ((uintptr_t)cu_seqlens % 4) return FA_ERR_ALIGN;
+  if (!std::isfinite(scale) || scale < 0.f || !std::isfinite((float)(scale * kLog2e)))
+    return FA_ERR_SCALE;
+  const int64_t rs = (int64_t)heads * d_k;  // row stride, elements
+  if (((int64_t)max_seqlen + 256) * rs * 2 > INT32_MAX) return FA_ERR_OVERFLOW;
+  const int64_t bh = (int64_t)batch * heads;
+  if (bh > kMaxGrid || bh * (((int64_t)max_seqlen + 127) / 128) > kMaxGrid) return FA_ERR_OVERFLOW;
+  if ((int64_t)total * rs > (INT64_C(1) << 50)) return FA_ERR_OVERFLOW;
+  const BwdLayout wl = bwd_layout(1, heads, total);
+  if (workspace_bytes < wl.total) return FA_ERR_SHAPE;
+  const uintptr_t t_sz = (uintptr_t)(total * rs * 2);
+  const Range ins[7] = {{(uintptr_t)q, (uintptr_t)q + t_sz},       {(uintptr_t)k, (uintptr_t)k + t_sz},
+                        {(uintptr_t)v, (uintptr_t)v + t_sz},       {(uintptr_t)o, (uintptr_t)o + t_sz},
+                        {(uintptr_t)dout, (uintptr_t)dout + t_sz},
+                        {(uintptr_t)lse, (uintptr_t)lse + (uintptr_t)((int64_t)heads * total * 4)},
+                        {(uintptr_t)cu_seqlens, (uintptr_t)cu_seqlens + (uintptr_t)(batch + 1) * 4}};
+  const Range outs[4] = {{(uintptr_t)dq, (uintptr_t)dq + t_sz},
+                         {(uintptr_t)dk, (uintptr_t)dk + t_sz},
+                         {(uintptr_t)dv, (uintptr_t)dv + t_sz},
+                         {(uintptr_t)workspace, (uintptr_t)workspace + wl.total}};
+  for (int i = 0; i < 4; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return FA_ERR_ALIAS;
   }
-  if (e != hipSuccess) {
-    g_last_hip_error = (int)e;
-    return FA_ERR_HIP;
-  }
-  return FA_OK;
+  if (total == 0) return FA_OK;  // no rows: nothing to compute
+  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, batch, heads, max_seqlen, d_k, scale, causal,
+                 dtype, workspace, cu_seqlens, total, stream);
 }
 
 const char* fa_status_string(int status) {

@@ -86,6 +86,58 @@ __device__ inline float dot8(u32x4_t a, u32x4_t b) {
   return s;
 }
 
+// One (batch, head), or one sequence of a ragged batch: row 0 of each
+// [rows, d] array, the byte row stride they share, the row count and row 0
+// of the per-row statistics (LSE, D, -LSE log2 e). Ragged offsets are clamped
+// to [0, total] and lengths to n, so no cu_seqlens content sends an access
+// outside the arrays.
+struct BwdView {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const uint8_t* o;
+  const uint8_t* g;
+  uint8_t* dq;
+  uint8_t* dk;
+  uint8_t* dv;
+  uint32_t rs;
+  int n;
+  const float* lse;
+  float* delta;
+  float* nlse2;
+};
+__device__ inline BwdView bwd_view(const BwdArgs& a, int bh) {
+  int n = a.n;
+  int64_t row0;   // element offset of row 0
+  size_t st0;     // index of row 0's statistics
+  if (a.cu_seqlens) {
+    const int b = bh / a.heads, h = bh - b * a.heads;
+    const int s0 = min(max(a.cu_seqlens[b], 0), a.total);
+    const int s1 = min(max(a.cu_seqlens[b + 1], s0), a.total);
+    n = min(s1 - s0, a.n);
+    row0 = ((int64_t)s0 * a.heads + h) * a.d;
+    st0 = (size_t)h * a.total + s0;
+  } else {
+    row0 = (int64_t)bh * a.n * a.d;
+    st0 = (size_t)bh * a.n;
+  }
+  BwdView v;
+  v.q = (const uint8_t*)a.q + row0 * 2;
+  v.k = (const uint8_t*)a.k + row0 * 2;
+  v.v = (const uint8_t*)a.v + row0 * 2;
+  v.o = (const uint8_t*)a.o + row0 * 2;
+  v.g = (const uint8_t*)a.dout + row0 * 2;
+  v.dq = (uint8_t*)a.dq + row0 * 2;
+  v.dk = (uint8_t*)a.dk + row0 * 2;
+  v.dv = (uint8_t*)a.dv + row0 * 2;
+  v.rs = (uint32_t)(a.rs * 2);
+  v.n = n;
+  v.lse = a.lse + st0;
+  v.delta = a.delta + st0;
+  v.nlse2 = a.nlse2 + st0;
+  return v;
+}
+
 // 32 columns (one per lane, rows 4 per register group) of a d-major
 // accumulator -> 8-byte stores of 4 consecutive d values: acc[db][4g + r] is
 // d-column db*32 + 8g + 4*hl + r of this lane's row.
@@ -133,19 +185,20 @@ void bwd_dq(BwdArgs a) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 31, hl = lane >> 5;
-  const int n = a.n;
-  const int tiles = (n + kDqBq - 1) / kDqBq;
+  const int tiles = (a.n + kDqBq - 1) / kDqBq;
   const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
+  const BwdView hv = bwd_view(a, tl.bh);
+  const int n = hv.n;
   const int q0 = tl.t * kDqBq;
+  if (q0 >= n) return;  // a tile past a short sequence (uniform)
   const int qw0 = q0 + 32 * w;
   const int qrow = qw0 + lr;
-  const size_t head_off = (size_t)tl.bh * (size_t)n * D;
-  const uint32_t head_bytes = (uint32_t)n * ROWB;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint8_t*)a.q + head_off * 2, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint8_t*)a.k + head_off * 2, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint8_t*)a.v + head_off * 2, head_bytes);
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc((const uint8_t*)a.o + head_off * 2, head_bytes);
-  const __amdgpu_buffer_rsrc_t rg = make_rsrc((const uint8_t*)a.dout + head_off * 2, head_bytes);
+  const uint32_t span = span_bytes(n, hv.rs, ROWB);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(hv.q, span);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(hv.k, span);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(hv.v, span);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(hv.o, span);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(hv.g, span);
 
   const int nt = ((CAUSAL ? min(q0 + kDqBq, n) : n) + BK - 1) / BK;  // key tiles 0 .. nt-1
 
@@ -154,10 +207,10 @@ void bwd_dq(BwdArgs a) {
   for (int i = 0; i < LPW; ++i) {
     const int byte = (w * LPW + i) * 1024 + lane * 16;
     const int row = byte / ROWB, p = (byte % ROWB) / 16;
-    off[i] = (uint32_t)(row * ROWB + (p ^ swz2<D>(row)) * 16);
+    off[i] = (uint32_t)row * hv.rs + (uint32_t)((p ^ swz2<D>(row)) * 16);
   }
   auto issue = [&](PairSlot<TILE_B>& slot, int t) __attribute__((always_inline)) {
-    const uint32_t base = t < nt ? (uint32_t)t * TILE_B : 0x80000000u;
+    const uint32_t base = t < nt ? (uint32_t)(t * BK) * hv.rs : 0x80000000u;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       lds_dma16(rk, slot.a + (w * LPW + i) * 1024, base + off[i]);
@@ -170,17 +223,16 @@ void bwd_dq(BwdArgs a) {
   float dpart = 0.f;
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    const uint32_t o_ = ((uint32_t)qrow * D + ks * 16 + hl * 8) * 2;
+    const uint32_t o_ = (uint32_t)qrow * hv.rs + (ks * 16 + hl * 8) * 2;
     qf[ks] = bload16(rq, o_);
     gf[ks] = bload16(rg, o_);
     dpart += dot8<IN>(gf[ks], bload16(ro, o_));
   }
   const float dsum = pair_sum(dpart);
-  const size_t srow = (size_t)tl.bh * n + qrow;
-  const float nl2 = qrow < n ? -a.lse[srow] * kLog2e : 0.f;
+  const float nl2 = qrow < n ? -hv.lse[qrow] * kLog2e : 0.f;
   if (hl == 0 && qrow < n) {
-    a.delta[srow] = dsum;
-    a.nlse2[srow] = nl2;
+    hv.delta[qrow] = dsum;
+    hv.nlse2[qrow] = nl2;
   }
   wait_vmcnt<0>();
 
@@ -279,7 +331,7 @@ void bwd_dq(BwdArgs a) {
   }
   wait_vmcnt<0>();
 
-  if (qrow < n) store_rows<IN, NDB>((uint16_t*)a.dq + head_off + (size_t)qrow * D, hl, dq, a.scale);
+  if (qrow < n) store_rows<IN, NDB>((uint16_t*)hv.dq + (size_t)qrow * (hv.rs / 2), hl, dq, a.scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -319,21 +371,22 @@ void bwd_dkdv(BwdArgs a) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 31, hl = lane >> 5;
-  const int n = a.n;
-  const int ktiles = (n + kKvBk - 1) / kKvBk;
+  const int ktiles = (a.n + kKvBk - 1) / kKvBk;
   // ascending key tiles: under a causal mask the first ones see the most queries
   const TileId tl = tile_of_block(blockIdx.x, a.bh, ktiles, false);
+  const BwdView hv = bwd_view(a, tl.bh);
+  const int n = hv.n;
   const int k0 = tl.t * kKvBk;
+  if (k0 >= n) return;  // a tile past a short sequence (uniform)
   const int kw0 = k0 + 32 * w;
   const int key = kw0 + lr;
-  const size_t head_off = (size_t)tl.bh * (size_t)n * D;
-  const uint32_t head_bytes = (uint32_t)n * ROWB;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint8_t*)a.q + head_off * 2, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint8_t*)a.k + head_off * 2, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint8_t*)a.v + head_off * 2, head_bytes);
-  const __amdgpu_buffer_rsrc_t rg = make_rsrc((const uint8_t*)a.dout + head_off * 2, head_bytes);
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.nlse2 + (size_t)tl.bh * n, (uint32_t)n * 4);
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.delta + (size_t)tl.bh * n, (uint32_t)n * 4);
+  const uint32_t span = span_bytes(n, hv.rs, ROWB);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(hv.q, span);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(hv.k, span);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(hv.v, span);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(hv.g, span);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(hv.nlse2, (uint32_t)n * 4);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(hv.delta, (uint32_t)n * 4);
 
   const int i_lo = CAUSAL ? k0 / kKvBq : 0;  // query tiles i_lo .. nt-1
   const int nt = (n + kKvBq - 1) / kKvBq;
@@ -343,13 +396,13 @@ void bwd_dkdv(BwdArgs a) {
   for (int i = 0; i < LPW; ++i) {
     const int byte = (w * LPW + i) * 1024 + lane * 16;
     const int row = byte / ROWB, p = (byte % ROWB) / 16;
-    off[i] = (uint32_t)(row * ROWB + (p ^ swz2<D>(row)) * 16);
+    off[i] = (uint32_t)row * hv.rs + (uint32_t)((p ^ swz2<D>(row)) * 16);
   }
   // Every wave copies the statistics too (the same bytes), so that all waves
   // issue the same number of loads per tile.
   auto issue = [&](QSlot<TILE_B>& slot, int t) __attribute__((always_inline)) {
     const bool in = t < nt;
-    const uint32_t base = in ? (uint32_t)t * TILE_B : 0x80000000u;
+    const uint32_t base = in ? (uint32_t)(t * kKvBq) * hv.rs : 0x80000000u;
     const uint32_t sbase = in ? (uint32_t)t * (kKvBq * 4) : 0x80000000u;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
@@ -364,7 +417,7 @@ void bwd_dkdv(BwdArgs a) {
   u32x4_t kf[NKS], vf[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    const uint32_t o_ = ((uint32_t)key * D + ks * 16 + hl * 8) * 2;
+    const uint32_t o_ = (uint32_t)key * hv.rs + (ks * 16 + hl * 8) * 2;
     kf[ks] = bload16(rk, o_);
     vf[ks] = bload16(rv, o_);
   }
@@ -490,8 +543,8 @@ void bwd_dkdv(BwdArgs a) {
   wait_vmcnt<0>();
 
   if (key < n) {
-    store_rows<IN, NDB>((uint16_t*)a.dv + head_off + (size_t)key * D, hl, dv, 1.0f);
-    store_rows<IN, NDB>((uint16_t*)a.dk + head_off + (size_t)key * D, hl, dk, a.scale);
+    store_rows<IN, NDB>((uint16_t*)hv.dv + (size_t)key * (hv.rs / 2), hl, dv, 1.0f);
+    store_rows<IN, NDB>((uint16_t*)hv.dk + (size_t)key * (hv.rs / 2), hl, dk, a.scale);
   }
 }
 

@@ -112,6 +112,11 @@ __device__ inline u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 __device__ inline u32x2_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
+// Bytes a buffer resource must cover for `rows` rows of `row_bytes` at a
+// stride of `rs` bytes (0 rows: nothing).
+__device__ inline uint32_t span_bytes(int rows, uint32_t rs, int row_bytes) {
+  return rows > 0 ? (uint32_t)(rows - 1) * rs + (uint32_t)row_bytes : 0u;
+}
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 

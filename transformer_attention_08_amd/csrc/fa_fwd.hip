@@ -111,11 +111,6 @@ __device__ inline HeadView head_view(const FwdArgs& a, int bh) {
   v.lse = !a.lse ? nullptr : a.cu_seqlens ? a.lse + (size_t)h * a.total + start : a.lse + (size_t)bh * a.n;
   return v;
 }
-// Bytes a buffer resource must cover for `rows` rows of `row_bytes` at a
-// stride of `rs` bytes (0 rows: nothing).
-__device__ inline uint32_t span_bytes(int rows, uint32_t rs, int row_bytes) {
-  return rows > 0 ? (uint32_t)(rows - 1) * rs + (uint32_t)row_bytes : 0u;
-}
 
 // Split-KV partial result of one row (lane halves hold d-columns as in the
 // O^T accumulator): O_g = o / l (times o_mult), LSE_g; zeros and -inf when

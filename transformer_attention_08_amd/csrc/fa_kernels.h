@@ -72,8 +72,17 @@ struct BwdArgs {
   void* dk;
   void* dv;
   int bh;
-  int n;
+  int n;           // rows per (batch, head); the longest sequence with cu_seqlens
   int d;
+  // Row stride (elements) shared by q, k, v, o, dout, dq, dk, dv: d for the
+  // dense [bh][n][d] layout, heads * d for packed [total][heads][d] rows.
+  int heads;
+  int64_t rs;
+  // Ragged batches (as FwdArgs): sequence b is rows cu_seqlens[b] ..
+  // cu_seqlens[b+1] of `total` packed rows; lse and the workspace rows are
+  // then [heads][total].
+  const int* cu_seqlens;
+  int total;
   bool causal;
   float c;            // scale * log2(e)
   float scale;
