@@ -38,7 +38,7 @@ METRIC = "attn fwd TFLOP/s & % of bf16 MFMA peak (h32, n8192, d_k128, causal)"
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "fp8": 5033.2, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 # the kernel each input type runs on
-KERNEL_OF_DTYPE = {"bf16": "fwd_direct", "f16": "fwd_direct", "fp8": "fwd_mfma16", "f32": "fwd_mfma32"}
+KERNEL_OF_DTYPE = {"bf16": "fwd_direct", "f16": "fwd_direct", "fp8": "fwd_direct8", "f32": "fwd_mfma32"}
 # the files the forward kernels and their launch shape are compiled from; a
 # stored traffic measurement is valid only for the sources it was taken on
 KERNEL_SOURCES = ("transformer_attention_08_amd/csrc/fa_fwd.hip",

@@ -144,318 +144,12 @@ __device__ inline uint32_t e4m3x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// ---------------------------------------------------------------------------
-// 16-bit and fp8 kernel. IN: element type of q/k/v. Both products run on the
-// 16-bit MFMA: f16 for F16 input, bf16 otherwise. FP8 (e4m3) inputs are
-// widened exactly to bf16 on their way into registers (Q) and LDS (K, V):
-// the fp8 MFMA sums its products with about 3e-5 relative error, which at
-// scores near 100 puts the log-sum-exp off by more than 1e-3, while the bf16
-// MFMA accumulates these same exact products in full fp32 precision.
-//
-// Pipeline. Iteration j applies the softmax to the scores of key tile j
-// (computed one iteration earlier) while the MFMA pipe already computes the
-// scores of tile j+1, then accumulates P_j V_j. K therefore runs one tile
-// ahead of V through the two LDS slots of each: during iteration j the waves
-// read K_{j+1} and V_j and the staged K_{j+2} and V_{j+1} are written into
-// the other slots, so one barrier per iteration suffices.
-//
-// Lazy rescale. The reference max m of a row only moves when a tile's max
-// exceeds it by more than kLazy (log2 units), so p <= 2^kLazy and o and l
-// are rescaled rarely. The result is unchanged: m cancels in o / l, and the
-// log-sum-exp is m + log2(l) for whatever m was used.
-// ---------------------------------------------------------------------------
+// Lazy rescale (all kernels). The reference max m of a row only moves when a
+// tile's max exceeds it by more than kLazy (log2 units), so p <= 2^kLazy and
+// o and l are rescaled rarely. The result is unchanged: m cancels in o / l,
+// and the log-sum-exp is m + log2(l) for whatever m was used.
 constexpr float kLazy = 8.0f;
 
-// Keys per K/V tile of the 16-bit kernel (32 or 64) and its waves per SIMD.
-#ifndef FA_TILE_KEYS
-#define FA_TILE_KEYS 32
-#endif
-#ifndef FA_WAVES_PER_SIMD
-#define FA_WAVES_PER_SIMD 2
-#endif
-
-template <Elt IN, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(FA_WAVES_PER_SIMD, FA_WAVES_PER_SIMD)))
-void fwd_mfma16(FwdArgs a) {
-  constexpr bool F8 = IN == Elt::FP8;
-  constexpr Elt PE = IN == Elt::F16 ? Elt::F16 : Elt::BF16;  // MFMA / LDS / O element type
-  constexpr int GB = F8 ? 1 : 2;       // bytes per q/k/v element in global memory
-  // keys per tile (fp8 with d_k 64 needs 64 keys to give every thread a chunk)
-  constexpr int BK = (F8 && D == 64) ? 64 : FA_TILE_KEYS;
-  constexpr int KB = BK / 32;          // 32-key blocks per tile
-  constexpr int KS = D + 8;            // K row stride in LDS, 16-bit elements
-  constexpr int VS = BK + 8;           // V^T row stride in LDS, 16-bit elements
-  constexpr int K_BYTES = BK * KS * 2;
-  constexpr int V_BYTES = D * VS * 2;
-  constexpr int CH = 16 / GB;          // elements per 16-byte global chunk
-  constexpr int CPR = D / CH;          // chunks per row
-  constexpr int NLD = BK * CPR / kThreads;  // chunks per thread per tile (K and V alike)
-  constexpr int VGRP = BK / NLD;       // V row groups per tile
-  constexpr int NKS = D / 16;          // MFMA k-steps of Q K^T
-  constexpr int NDB = D / 32;          // 32-column blocks of O
-  static_assert(NLD >= 1 && NLD <= 4 && CPR * VGRP == kThreads, "tile mapping");
-  static_assert(K_BYTES % 16 == 0 && V_BYTES % 16 == 0, "LDS alignment");
-
-  // [K slot 0][K slot 1][V^T slot 0][V^T slot 1]
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * K_BYTES + 2 * V_BYTES];
-  uint8_t* const kls = smem;
-  uint8_t* const vls = smem + 2 * K_BYTES;
-
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, provably uniform
-  const int lane = tid & 63, lr = lane & 31, hl = lane >> 5;
-  const int tiles = (a.n + kBq - 1) / kBq;
-  const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
-  const HeadView hv = head_view<GB, 2>(a, tl.bh);
-  const int n = hv.n;
-  const int q0 = tl.t * kBq;
-  if (q0 >= n) return;                // a tile past a short sequence (uniform)
-  const int qw0 = q0 + 32 * w;        // first query row of this wave
-  const int qrow = qw0 + lr;          // query row of this lane
-
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(hv.q, span_bytes(n, hv.qrs, D * GB));
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(hv.k, span_bytes(n, hv.krs, D * GB));
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(hv.v, span_bytes(n, hv.vrs, D * GB));
-
-  // Q fragments (B operand of S^T = K Q^T): lane holds query qrow, d-columns
-  // ks*16 + hl*8 .. +8 for each k-step ks. Rows past n load as zeros.
-  u32x4_t qf[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    const uint32_t off = (uint32_t)qrow * hv.qrs + (ks * 16 + hl * 8) * GB;
-    if constexpr (F8) {
-      const u32x2_t b = bload8(rq, off);
-      qf[ks] = u32x4_t{e4m3x2_to_bf16x2<false>(b[0]), e4m3x2_to_bf16x2<true>(b[0]),
-                       e4m3x2_to_bf16x2<false>(b[1]), e4m3x2_to_bf16x2<true>(b[1])};
-    } else {
-      qf[ks] = bload16(rq, off);
-    }
-  }
-
-  const KeyTiles kt = key_tiles<BK>(a, n, min(q0 + kBq, n), CAUSAL);
-  const int j_lo = kt.lo, nt = kt.hi;  // key tiles j_lo .. nt-1
-
-  // ---- staging of global tiles through registers
-  u32x4_t kst[NLD], vst[NLD];
-  const int vgrp = tid % VGRP, vch = tid / VGRP;  // V: rows NLD*vgrp.., chunk vch
-
-  auto load_k = [&](int j) {
-#pragma unroll
-    for (int it = 0; it < NLD; ++it) {
-      const int idx = tid + it * kThreads;
-      const int row = idx / CPR, c = idx % CPR;
-      kst[it] = bload16(rk, (uint32_t)(j * BK + row) * hv.krs + c * 16);
-    }
-  };
-  auto load_v = [&](int j) {
-#pragma unroll
-    for (int r = 0; r < NLD; ++r) {
-      const int key = j * BK + NLD * vgrp + r;
-      vst[r] = bload16(rv, (uint32_t)key * hv.vrs + vch * 16);
-    }
-  };
-  auto store_k = [&](int slot) {
-    uint8_t* kl = kls + slot * K_BYTES;
-#pragma unroll
-    for (int it = 0; it < NLD; ++it) {
-      const int idx = tid + it * kThreads;
-      const int row = idx / CPR, c = idx % CPR;
-      uint8_t* dst = kl + (row * KS + c * CH) * 2;
-      if constexpr (F8) {
-        const u32x4_t x = kst[it];
-        *(u32x4_t*)dst = u32x4_t{e4m3x2_to_bf16x2<false>(x[0]), e4m3x2_to_bf16x2<true>(x[0]),
-                                 e4m3x2_to_bf16x2<false>(x[1]), e4m3x2_to_bf16x2<true>(x[1])};
-        *(u32x4_t*)(dst + 16) = u32x4_t{e4m3x2_to_bf16x2<false>(x[2]), e4m3x2_to_bf16x2<true>(x[2]),
-                                        e4m3x2_to_bf16x2<false>(x[3]), e4m3x2_to_bf16x2<true>(x[3])};
-      } else {
-        *(u32x4_t*)dst = kst[it];
-      }
-    }
-  };
-  auto store_v = [&](int slot) {
-    // V^T: row d, keys contiguous. vw[r][i] holds 16-bit elements 2i, 2i+1
-    // of this thread's chunk of key row NLD*vgrp + r.
-    uint32_t vw[NLD][CH / 2];
-#pragma unroll
-    for (int r = 0; r < NLD; ++r) {
-#pragma unroll
-      for (int i = 0; i < CH / 2; ++i) {
-        if constexpr (F8)
-          vw[r][i] = (i & 1) ? e4m3x2_to_bf16x2<true>(vst[r][i / 2])
-                             : e4m3x2_to_bf16x2<false>(vst[r][i / 2]);
-        else
-          vw[r][i] = vst[r][i];
-      }
-    }
-    uint16_t* vt = (uint16_t*)(vls + slot * V_BYTES);
-#pragma unroll
-    for (int dd = 0; dd < CH; ++dd) {
-      uint16_t* dst = vt + (vch * CH + dd) * VS + NLD * vgrp;
-      const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-      if constexpr (NLD == 4) {
-        const uint32_t x0 = __builtin_amdgcn_perm(vw[1][dd / 2], vw[0][dd / 2], sel);
-        const uint32_t x1 = __builtin_amdgcn_perm(vw[3][dd / 2], vw[2][dd / 2], sel);
-        *(u32x2_t*)dst = u32x2_t{x0, x1};
-      } else if constexpr (NLD == 2) {
-        *(uint32_t*)dst = __builtin_amdgcn_perm(vw[1][dd / 2], vw[0][dd / 2], sel);
-      } else {
-        *dst = (uint16_t)((dd & 1) ? (vw[0][dd / 2] >> 16) : (vw[0][dd / 2] & 0xffffu));
-      }
-    }
-  };
-
-  // ---- the two MFMA stages and the softmax
-  const int krow = perm32(lr);
-  auto scores = [&](int slot, f32x16_t (&s)[KB]) {
-    const uint8_t* kl = kls + slot * K_BYTES;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16_t{};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const u32x4_t av = *(const u32x4_t*)(kl + ((kb * 32 + krow) * KS + ks * 16 + hl * 8) * 2);
-        s[kb] = mfma16<PE>(av, qf[ks], s[kb]);
-      }
-    }
-  };
-
-  const float c = a.c;
-  float m2 = -INFINITY;  // reference max of c * s (base-2 units) for this row
-  float lp = 0.f;        // this lane's part of the running sum l
-  f32x16_t o[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) o[db] = f32x16_t{};
-
-  // Softmax of one score tile into packed P, with the lazy rescale of o, l.
-  auto softmax = [&](f32x16_t (&s)[KB], u32x4_t (&pb)[KB][2]) {
-    float mx = s[0][0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
-#pragma unroll
-    for (int kb = 1; kb < KB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = pair_max(mx);
-    const float mc = mx * c;
-    const bool up = mc > m2 + kLazy;
-    const float m_use = up ? mc : m2;
-    const float alpha = fast_exp2(m2 - exp_ref(m_use));
-    const float nm = -exp_ref(m_use);
-    float ls = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(s[kb][i], c, nm));
-        const float p1 = fast_exp2(__builtin_fmaf(s[kb][i + 1], c, nm));
-        ls += p0 + p1;
-        pb[kb][i >> 3][(i & 7) >> 1] = pack2<PE>(p0, p1);
-      }
-    }
-    lp = __builtin_fmaf(alpha, lp, ls);
-    m2 = m_use;
-    if (__any(up)) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-    }
-  };
-
-  auto mask = [&](f32x16_t (&s)[KB], int kbase) {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kbase + kb * 32 + 16 * (i >> 3) + 8 * hl + (i & 7);
-        const bool ok = key < n && (!CAUSAL || key <= qrow);
-        s[kb][i] = ok ? s[kb][i] : -INFINITY;
-      }
-    }
-  };
-
-  auto pv = [&](int slot, const u32x4_t (&pb)[KB][2]) {
-    const uint16_t* vt = (const uint16_t*)(vls + slot * V_BYTES);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const u32x4_t av = *(const u32x4_t*)(vt + (db * 32 + lr) * VS + kb * 32 + 16 * s2 + 8 * hl);
-          o[db] = mfma16<PE>(av, pb[kb][s2], o[db]);
-        }
-      }
-    }
-  };
-
-  const bool wave_live = qw0 < n;
-  // tile j holds keys the wave can see
-  auto live = [&](int j) { return j < nt && wave_live && !(CAUSAL && j * BK > qw0 + 31); };
-  auto needs_mask = [&](int j) { return (j * BK + BK > n) || (CAUSAL && j * BK + BK - 1 > qw0); };
-
-  // Prologue: K, V of tile j_lo and K of tile j_lo + 1 into LDS; S of j_lo.
-  // Slots are indexed relative to j_lo.
-  load_k(j_lo);
-  load_v(j_lo);
-  store_k(0);
-  store_v(0);
-  if (nt > j_lo + 1) {
-    load_k(j_lo + 1);
-    store_k(1);
-  }
-  __syncthreads();
-  f32x16_t s[KB];
-  if (live(j_lo)) scores(0, s);
-  __syncthreads();  // K slot 0 is refilled during the first iteration
-
-  for (int j = j_lo; j < nt; ++j) {
-    const int r = j - j_lo;
-    const bool more_v = j + 1 < nt, more_k = j + 2 < nt;
-    if (more_v) load_v(j + 1);
-    if (more_k) load_k(j + 2);
-    const bool lj = live(j), ln = live(j + 1);
-    f32x16_t sn[KB];
-    u32x4_t pb[KB][2];
-    if (lj && ln && !needs_mask(j)) {
-      // steady state: scores of tile j+1 overlap the softmax of tile j
-      scores((r + 1) & 1, sn);
-      softmax(s, pb);
-    } else {
-      if (ln) scores((r + 1) & 1, sn);
-      if (lj) {
-        if (needs_mask(j)) mask(s, j * BK);
-        softmax(s, pb);
-      }
-    }
-    if (lj) pv(r & 1, pb);
-    if (more_v) store_v((r + 1) & 1);
-    if (more_k) store_k(r & 1);
-    __syncthreads();
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s[kb] = sn[kb];
-  }
-
-  // Epilogue: O = o / l once per row; LSE = ln 2 * (m2 + log2 l).
-  const float lt = pair_sum(lp);
-  if (qrow < n && a.part_o) {
-    store_partial<NDB>(a, tl.bh, qrow, hl, o, m2, lt);
-  } else if (qrow < n) {
-    const float inv = a.o_mult / lt;
-    uint16_t* Og = (uint16_t*)hv.o + (size_t)qrow * hv.ors;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = db * 32 + 8 * g + 4 * hl;
-        const uint32_t x0 = pack2<PE>(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
-        const uint32_t x1 = pack2<PE>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-        *(u32x2_t*)(Og + d) = u32x2_t{x0, x1};
-      }
-    }
-    if (hl == 0 && hv.lse) hv.lse[qrow] = (m2 + __log2f(lt)) * kLn2;
-  }
-}
 // ---------------------------------------------------------------------------
 // Direct-to-LDS kernel for f16 / bf16 inputs. Eight waves (256 query rows)
 // per workgroup, 128-key tiles, and an NS-stage ring (2 stages: 128 KiB of
@@ -733,6 +427,246 @@ void fwd_direct(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// e4m3 variant of fwd_direct. The buffer unit copies each K/V tile as e4m3
+// bytes into an LDS staging area (half the bytes of a bf16 tile). One step
+// before a tile is used, the waves widen it -- exactly, every e4m3 value is a
+// bf16 value -- into the swizzled ring layout of fwd_direct, whose compute
+// then runs on the bf16 MFMA (the fp8 MFMA accumulates with about 3e-5
+// relative error, too much for the LSE bar at scores near 100). Two barriers
+// per step: before the widening (the staged tile has landed; the target slot
+// is free) and after it (the slot is ready; the staging area is free for the
+// next copy). LDS: two bf16 slots plus the staging area, 160 KiB at d_k 128.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Stage8 {
+  __attribute__((aligned(1024))) uint8_t k[DirectLayout<D>::BK * D];
+  __attribute__((aligned(1024))) uint8_t v[DirectLayout<D>::BK * D];
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kDirectThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_direct8(FwdArgs a) {
+  using L = DirectLayout<D>;
+  constexpr int BK = L::BK, ROWB = L::ROWB, TILE_B = L::TILE_B;
+  constexpr int KB = BK / 32, NKS = D / 16, NDB = D / 32;
+  constexpr int STILE = BK * D;                         // bytes per staged e4m3 tile (K or V)
+  constexpr int SLPW = STILE / 1024 / kDirectWaves;     // 1 KiB copies per wave per tile
+  constexpr int SCPR = D / 16;                          // 16-byte e4m3 chunks per row
+  constexpr int CPT = STILE / 16 / kDirectThreads;      // staged chunks per thread
+  static_assert(SLPW >= 1 && CPT >= 1, "tile mapping");
+
+  __shared__ LdsSlot<TILE_B> ring0, ring1;
+  __shared__ Stage8<D> stage;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 31, hl = lane >> 5;
+  const int tiles = (a.n + kDirectBq - 1) / kDirectBq;
+  const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
+  const HeadView hv = head_view<1, 2>(a, tl.bh);
+  const int n = hv.n;
+  const int q0 = tl.t * kDirectBq;
+  if (q0 >= n) return;  // a tile past a short sequence (uniform)
+  const int qw0 = q0 + 32 * w;
+  const int qrow = qw0 + lr;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(hv.q, span_bytes(n, hv.qrs, D));
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(hv.k, span_bytes(n, hv.krs, D));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(hv.v, span_bytes(n, hv.vrs, D));
+
+  const KeyTiles kt = key_tiles<BK>(a, n, min(q0 + kDirectBq, n), CAUSAL);
+  const int j_lo = kt.lo, nt = kt.hi;
+
+  // staging copies: plain row-major e4m3 rows
+  uint32_t koff[SLPW], voff[SLPW];
+#pragma unroll
+  for (int i = 0; i < SLPW; ++i) {
+    const int byte = (w * SLPW + i) * 1024 + lane * 16;
+    const int row = byte / D, c = (byte % D) / 16;
+    koff[i] = (uint32_t)row * hv.krs + (uint32_t)(c * 16);
+    voff[i] = (uint32_t)row * hv.vrs + (uint32_t)(c * 16);
+  }
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const uint32_t kb = t < nt ? (uint32_t)(t * BK) * hv.krs : 0x80000000u;
+    const uint32_t vb = t < nt ? (uint32_t)(t * BK) * hv.vrs : 0x80000000u;
+#pragma unroll
+    for (int i = 0; i < SLPW; ++i) {
+      lds_dma16(rk, stage.k + (w * SLPW + i) * 1024, kb + koff[i]);
+      lds_dma16(rv, stage.v + (w * SLPW + i) * 1024, vb + voff[i]);
+    }
+  };
+  // widen the staged tile into a ring slot: 16 e4m3 values -> two 16-byte
+  // bf16 chunks at their swizzled places
+  auto widen = [&](LdsSlot<TILE_B>& slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = tid + i * kDirectThreads;
+      const int row = ch / SCPR, c = ch % SCPR;
+      const u32x4_t xk = *(const u32x4_t*)(stage.k + ch * 16);
+      const u32x4_t xv = *(const u32x4_t*)(stage.v + ch * 16);
+      const int ks = L::kswz(row), vs = L::vswz(row);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const u32x4_t bk = u32x4_t{e4m3x2_to_bf16x2<false>(xk[2 * e]), e4m3x2_to_bf16x2<true>(xk[2 * e]),
+                                   e4m3x2_to_bf16x2<false>(xk[2 * e + 1]), e4m3x2_to_bf16x2<true>(xk[2 * e + 1])};
+        const u32x4_t bv = u32x4_t{e4m3x2_to_bf16x2<false>(xv[2 * e]), e4m3x2_to_bf16x2<true>(xv[2 * e]),
+                                   e4m3x2_to_bf16x2<false>(xv[2 * e + 1]), e4m3x2_to_bf16x2<true>(xv[2 * e + 1])};
+        *(u32x4_t*)(slot.k + row * ROWB + (((2 * c + e) ^ ks) * 16)) = bk;
+        *(u32x4_t*)(slot.v + row * ROWB + (((2 * c + e) ^ vs) * 16)) = bv;
+      }
+    }
+  };
+
+  // Q fragments, widened once
+  u32x4_t qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const u32x2_t b = bload8(rq, (uint32_t)qrow * hv.qrs + (ks * 16 + hl * 8));
+    qf[ks] = u32x4_t{e4m3x2_to_bf16x2<false>(b[0]), e4m3x2_to_bf16x2<true>(b[0]),
+                     e4m3x2_to_bf16x2<false>(b[1]), e4m3x2_to_bf16x2<true>(b[1])};
+  }
+  wait_vmcnt<0>();
+
+  const int krow = perm32(lr);
+  const int kswz = L::kswz(krow);
+  const int grp = lane >> 4, li = lane & 15;
+  const int vrow0 = 8 * hl + (li >> 2);
+  const int vswz = L::vswz(vrow0);
+  const int vcol = 16 * (grp & 1) + 4 * (li & 3);
+
+  const float c = a.c;
+  float m2 = -INFINITY, lp = 0.f;
+  f32x16_t o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = f32x16_t{};
+  const bool wave_live = qw0 < n;
+  auto live = [&](int j) __attribute__((always_inline)) { return wave_live && !(CAUSAL && j * BK > qw0 + 31); };
+  auto needs_mask = [&](int j) __attribute__((always_inline)) { return (j * BK + BK > n) || (CAUSAL && j * BK + BK - 1 > qw0); };
+
+  // the compute of fwd_direct on the widened tile
+  auto compute = [&](const LdsSlot<TILE_B>& slot, int j) __attribute__((always_inline)) {
+    f32x16_t s[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4_t av = *(const u32x4_t*)(slot.k + (kb * 32 + krow) * ROWB + (((2 * ks + hl) ^ kswz) * 16));
+        s[kb] = mfma16<Elt::BF16>(av, qf[ks], s[kb]);
+      }
+    }
+    if (needs_mask(j)) {
+      const int kbase = j * BK;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kbase + kb * 32 + 16 * (i >> 3) + 8 * hl + (i & 7);
+          const bool ok = key < n && (!CAUSAL || key <= qrow);
+          s[kb][i] = ok ? s[kb][i] : -INFINITY;
+        }
+      }
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+    for (int kb = 1; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = pair_max(mx);
+    const float mc = mx * c;
+    const bool up = mc > m2 + kLazy;
+    const float m_use = up ? mc : m2;
+    const float alpha = fast_exp2(m2 - exp_ref(m_use));
+    const float nm = -exp_ref(m_use);
+    float ls = 0.f;
+    u32x4_t pb[KB][2];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[kb][i], c, nm));
+        const float p1 = fast_exp2(__builtin_fmaf(s[kb][i + 1], c, nm));
+        ls += p0 + p1;
+        pb[kb][i >> 3][(i & 7) >> 1] = pack2<Elt::BF16>(p0, p1);
+      }
+    }
+    lp = __builtin_fmaf(alpha, lp, ls);
+    m2 = m_use;
+    if (__any(up)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int row = kb * 32 + 16 * s2 + vrow0;
+          const int col = db * 32 + vcol;
+          const uint8_t* p0 = slot.v + row * ROWB + (((col >> 3) ^ vswz) * 16) + ((col & 4) << 1);
+          const u32x2_t lo = lds_read_tr16(p0);
+          const u32x2_t hi = lds_read_tr16(p0 + 4 * ROWB);
+          o[db] = mfma16<Elt::BF16>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pb[kb][s2], o[db]);
+        }
+      }
+    }
+  };
+
+  // Step j: tile j is in `cur`; tile j + 1 is staged; tile j + 2 is copied next.
+  auto step = [&](LdsSlot<TILE_B>& cur, LdsSlot<TILE_B>& nxt, int j) __attribute__((always_inline)) {
+    wait_vmcnt<0>();   // this wave's share of tile j + 1 is staged
+    __syncthreads();   // ... every wave's; nobody reads tile j - 1 from nxt any more
+    if (j + 1 < nt) widen(nxt);
+    __syncthreads();   // nxt holds tile j + 1; the staging area is free
+    issue(j + 2);
+    if (live(j)) compute(cur, j);
+  };
+
+  {
+    LdsSlot<TILE_B>* slots[2] = {&ring0, &ring1};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4_t* p = (u32x4_t*)slots[s];
+      for (int i = tid; i < (int)(sizeof(LdsSlot<TILE_B>) / 16); i += kDirectThreads)
+        p[i] = u32x4_t{0, 0, 0, 0};
+    }
+  }
+  issue(j_lo);
+  wait_vmcnt<0>();
+  __syncthreads();
+  widen(ring0);
+  __syncthreads();
+  issue(j_lo + 1);
+  for (int j0 = j_lo; j0 < nt; j0 += 2) {
+    step(ring0, ring1, j0);
+    if (j0 + 1 < nt) step(ring1, ring0, j0 + 1);
+  }
+  wait_vmcnt<0>();
+
+  const float lt = pair_sum(lp);
+  if (qrow < n && a.part_o) {
+    store_partial<NDB>(a, tl.bh, qrow, hl, o, m2, lt);
+  } else if (qrow < n) {
+    const float inv = a.o_mult / lt;
+    uint16_t* Og = (uint16_t*)hv.o + (size_t)qrow * hv.ors;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + 8 * g + 4 * hl;
+        const uint32_t x0 = pack2<Elt::BF16>(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+        const uint32_t x1 = pack2<Elt::BF16>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+        *(u32x2_t*)(Og + d) = u32x2_t{x0, x1};
+      }
+    }
+    if (hl == 0 && hv.lse) hv.lse[qrow] = (m2 + __log2f(lt)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 kernel (32x32x2 fp32 MFMA, 32-key tiles). Same structure and register
 // layout as above; with one element per operand lane the P.V step reads V
 // rows straight from a row-major LDS tile, so no transpose is needed.
@@ -975,7 +909,8 @@ hipError_t dispatch_causal(const FwdArgs& a, hipStream_t s) {
   if constexpr (E == Elt::F32) {
     return a.causal ? launch(fwd_mfma32<D, true>, a, s) : launch(fwd_mfma32<D, false>, a, s);
   } else if constexpr (E == Elt::FP8) {
-    return a.causal ? launch(fwd_mfma16<E, D, true>, a, s) : launch(fwd_mfma16<E, D, false>, a, s);
+    return a.causal ? launch(fwd_direct8<D, true>, a, s, kDirectBq, kDirectThreads)
+                    : launch(fwd_direct8<D, false>, a, s, kDirectBq, kDirectThreads);
   } else {
     return a.causal ? launch(fwd_direct<E, D, true>, a, s, kDirectBq, kDirectThreads)
                     : launch(fwd_direct<E, D, false>, a, s, kDirectBq, kDirectThreads);
