@@ -9,9 +9,12 @@ Prints one JSON line with the throughput, the roofline position of the
 kernel (achieved TFLOP/s against the dense MFMA peak of its dtype, plus the
 HBM traffic measured by rocprofv3 counters when the stored measurement
 belongs to the current kernel source) and the CPU oracle timed on a bounded
-sample of the same workload on this host's cores.
+sample of the same workload on this host's cores. A second pass times ten
+calls one by one with 512 MiB of other device memory read before each, so
+that no input is served from the L2s or the 256 MB Infinity Cache
+(`cold_cache`).
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--n N] [--splits S] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--n N] [--splits S] [--no-cpu-baseline] [--no-cold-cache]
     python bench.py --backward      # fa_backward on the workload
     python bench.py --unfused       # the unfused contrast (S, P in memory)
     python bench.py --layout bshd   # [batch, n, heads, d_k] inputs (fa_forward_strided)
@@ -175,6 +178,30 @@ def time_steps(step, stream, steps, warmup):
     return evs[0].elapsed_time(evs[-1]) / steps, per
 
 
+def cold_cache_pass(step, stream, flops, calls=10, scrub_bytes=512 << 20):
+    """Per-call timing with scrub_bytes of device memory read before every
+    call, so that no input is left in the L2s or the 256 MB Infinity Cache.
+    The scrub reads (a sum) rather than writes, so that the call does not
+    also pay for writing dirty scrub lines back; the events bracket the call
+    alone."""
+    import torch
+    scrub = torch.ones(scrub_bytes // 4, dtype=torch.float32, device="cuda")
+    acc = torch.zeros((), dtype=torch.float32, device="cuda")
+    per = []
+    for _ in range(calls):
+        torch.sum(scrub, out=acc)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1))
+    del scrub
+    ms = statistics.median(per)
+    return {"ms_median": round(ms, 5), "ms_min": round(min(per), 5),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "calls": calls, "scrub_bytes_read": scrub_bytes}
+
+
 def bench_backward(args, w):
     """One step = one fa_backward call (both passes) on the workload, with the
     forward's O and LSE computed once beforehand."""
@@ -312,6 +339,8 @@ def main(argv=None):
                     help="ragged batch of this many sequences (seeded log-normal lengths, "
                          "16 .. n rows) through fa_forward_varlen")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold-cache", action="store_true",
+                    help="skip the second pass that reads 512 MiB of other device memory before each call")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args(argv)
 
@@ -433,6 +462,8 @@ def main(argv=None):
                                 KERNEL_OF_DTYPE[w.dtype] + ("+combine_splits" if ws is not None else "")),
                      "min_hbm_bytes": min_hbm_bytes(w)},
     }
+    if not args.no_cold_cache:
+        line["cold_cache"] = cold_cache_pass(step, stream, flops)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(line), flush=True)
