@@ -261,12 +261,13 @@ void fwd_direct(FwdArgs a) {
     }
   };
 
-  // Q fragments (B operand of S^T = K Q^T), complete before the ring starts.
+  // Q fragments (B operand of S^T = K Q^T). They land while the ring is
+  // zeroed; loads complete in issue order, so the first step's wait for its
+  // tile covers them too.
   u32x4_t qf[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
     qf[ks] = bload16(rq, (uint32_t)qrow * hv.qrs + (ks * 16 + hl * 8) * 2);
-  wait_vmcnt<0>();
 
   // Per-lane LDS read offsets.
   const int krow = perm32(lr);
@@ -516,15 +517,12 @@ void fwd_direct8(FwdArgs a) {
     }
   };
 
-  // Q fragments, widened once
+  // Q fragments as e4m3; they land during the prologue and are widened once
+  // after its first wait
+  u32x2_t q8[NKS];
   u32x4_t qf[NKS];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    const u32x2_t b = bload8(rq, (uint32_t)qrow * hv.qrs + (ks * 16 + hl * 8));
-    qf[ks] = u32x4_t{e4m3x2_to_bf16x2<false>(b[0]), e4m3x2_to_bf16x2<true>(b[0]),
-                     e4m3x2_to_bf16x2<false>(b[1]), e4m3x2_to_bf16x2<true>(b[1])};
-  }
-  wait_vmcnt<0>();
+  for (int ks = 0; ks < NKS; ++ks) q8[ks] = bload8(rq, (uint32_t)qrow * hv.qrs + (ks * 16 + hl * 8));
 
   const int krow = perm32(lr);
   const int kswz = L::kswz(krow);
@@ -636,6 +634,10 @@ void fwd_direct8(FwdArgs a) {
   }
   issue(j_lo);
   wait_vmcnt<0>();
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    qf[ks] = u32x4_t{e4m3x2_to_bf16x2<false>(q8[ks][0]), e4m3x2_to_bf16x2<true>(q8[ks][0]),
+                     e4m3x2_to_bf16x2<false>(q8[ks][1]), e4m3x2_to_bf16x2<true>(q8[ks][1])};
   __syncthreads();
   widen(ring0);
   __syncthreads();
