@@ -189,7 +189,7 @@ def cold_cache_pass(step, stream, flops, calls=10, scrub_bytes=512 << 20):
     acc = torch.zeros((), dtype=torch.float32, device="cuda")
     per = []
     for _ in range(calls):
-        torch.sum(scrub, out=acc)
+        torch.sum(scrub, dim=0, out=acc)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         step()
