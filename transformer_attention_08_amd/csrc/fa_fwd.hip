@@ -185,6 +185,9 @@ constexpr int kDirectBq = 32 * kDirectWaves;
 #ifndef FA_STAGES
 #define FA_STAGES 2
 #endif
+#ifndef FA_PAIR_TILES
+#define FA_PAIR_TILES 1
+#endif
 
 template <int D>
 struct DirectLayout {
@@ -223,19 +226,28 @@ void fwd_direct(FwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, provably uniform
   const int lane = tid & 63, lr = lane & 31, hl = lane >> 5;
   const int tiles = (a.n + kDirectBq - 1) / kDirectBq;
-  const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
+  // Paired causal tiles: the workgroup takes query tile T-1-p, then tile p of
+  // the same head -- 2T + 2 key tiles in all, the same for every pair -- and
+  // its K/V ring runs on from the first tile's keys into the second's, so
+  // the second tile starts with its first keys already in LDS.
+  const bool pair = CAUSAL && a.pair;
+  const TileId tl = pair ? tile_of_block(blockIdx.x, a.bh, tiles / 2, false, tiles)
+                         : tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
   const HeadView hv = head_view<2, 2>(a, tl.bh);
   const int n = hv.n;
-  const int q0 = tl.t * kDirectBq;
+  int q0 = (pair ? tiles - 1 - tl.t : tl.t) * kDirectBq;
   if (q0 >= n) return;  // a tile past a short sequence (uniform)
-  const int qw0 = q0 + 32 * w;
-  const int qrow = qw0 + lr;
+  int qw0 = q0 + 32 * w;
+  int qrow = qw0 + lr;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(hv.q, span_bytes(n, hv.qrs, ROWB));
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(hv.k, span_bytes(n, hv.krs, ROWB));
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(hv.v, span_bytes(n, hv.vrs, ROWB));
 
   const KeyTiles kt = key_tiles<BK>(a, n, min(q0 + kDirectBq, n), CAUSAL);
-  const int j_lo = kt.lo, nt = kt.hi;  // key tiles j_lo .. nt-1 (ring slots relative to j_lo)
+  // Ring positions J run over j_lo .. nt-1: the key tiles of the (first) query
+  // tile, then, paired, those of the second (key tile J - nt0).
+  const int j_lo = kt.lo, nt0 = kt.hi;
+  const int nt = pair ? nt0 + key_tiles<BK>(a, n, min(tl.t * kDirectBq + kDirectBq, n), CAUSAL).hi : nt0;
 
   // Per-lane source offsets of this wave's share of a tile (tile 0).
   uint32_t koff[LPW], voff[LPW];
@@ -251,9 +263,10 @@ void fwd_direct(FwdArgs a) {
   // so every step issues the same number of loads. The copies are issued
   // through inline assembly: the compiler does not track them, and the
   // explicit vmcnt wait plus barrier in each step orders them.
-  auto issue = [&](LdsSlot<TILE_B>& slot, int t) __attribute__((always_inline)) {
-    const uint32_t kb = t < nt ? (uint32_t)(t * BK) * hv.krs : 0x80000000u;
-    const uint32_t vb = t < nt ? (uint32_t)(t * BK) * hv.vrs : 0x80000000u;
+  auto issue = [&](LdsSlot<TILE_B>& slot, int J) __attribute__((always_inline)) {
+    const int t = pair && J >= nt0 ? J - nt0 : J;
+    const uint32_t kb = J < nt ? (uint32_t)(t * BK) * hv.krs : 0x80000000u;
+    const uint32_t vb = J < nt ? (uint32_t)(t * BK) * hv.vrs : 0x80000000u;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       lds_dma16(rk, slot.k + (w * LPW + i) * 1024, kb + koff[i]);
@@ -265,9 +278,12 @@ void fwd_direct(FwdArgs a) {
   // zeroed; loads complete in issue order, so the first step's wait for its
   // tile covers them too.
   u32x4_t qf[NKS];
+  auto load_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks)
-    qf[ks] = bload16(rq, (uint32_t)qrow * hv.qrs + (ks * 16 + hl * 8) * 2);
+    for (int ks = 0; ks < NKS; ++ks)
+      qf[ks] = bload16(rq, (uint32_t)qrow * hv.qrs + (ks * 16 + hl * 8) * 2);
+  };
+  load_q();
 
   // Per-lane LDS read offsets.
   const int krow = perm32(lr);
@@ -282,8 +298,7 @@ void fwd_direct(FwdArgs a) {
   f32x16_t o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x16_t{};
-  const bool wave_live = qw0 < n;
-  auto live = [&](int j) __attribute__((always_inline)) { return wave_live && !(CAUSAL && j * BK > qw0 + 31); };
+  auto live = [&](int j) __attribute__((always_inline)) { return qw0 < n && !(CAUSAL && j * BK > qw0 + 31); };
   auto needs_mask = [&](int j) __attribute__((always_inline)) { return (j * BK + BK > n) || (CAUSAL && j * BK + BK - 1 > qw0); };
 
   auto compute = [&](const LdsSlot<TILE_B>& slot, int j) __attribute__((always_inline)) {
@@ -370,14 +385,54 @@ void fwd_direct(FwdArgs a) {
     else if constexpr (decltype(S)::value == 2) return ring2;
     else return ring3;
   };
-  // One step: tile j lives in slot S; the slot of tile j - 1 is refilled
-  // with tile j + NS - 1 once every wave is past tile j - 1.
-  auto step = [&](auto S, int j) __attribute__((always_inline)) {
+  // Epilogue of a query tile: O = o / l once per row; LSE = ln 2 * (m2 + log2 l).
+  auto finish = [&]() __attribute__((always_inline)) {
+    const float lt = pair_sum(lp);
+    if (qrow < n && a.part_o) {
+      store_partial<NDB>(a, tl.bh, qrow, hl, o, m2, lt);
+    } else if (qrow < n) {
+      const float inv = a.o_mult / lt;
+      uint16_t* Og = (uint16_t*)hv.o + (size_t)qrow * hv.ors;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = db * 32 + 8 * g + 4 * hl;
+          const uint32_t x0 = pack2<IN>(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+          const uint32_t x1 = pack2<IN>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+          *(u32x2_t*)(Og + d) = u32x2_t{x0, x1};
+        }
+      }
+      if (hl == 0 && hv.lse) hv.lse[qrow] = (m2 + __log2f(lt)) * kLn2;
+    }
+  };
+
+  // One step: ring position J (key tile J - base) lives in slot S; the slot
+  // of J - 1 is refilled with position J + NS - 1 once every wave is past
+  // J - 1.
+  auto step = [&](auto S, int J, int base) __attribute__((always_inline)) {
     using SN = std::integral_constant<int, (decltype(S)::value + NS - 1) % NS>;
-    wait_vmcnt<(NS - 2) * 2 * LPW>();  // this wave's share of tile j has landed
+    wait_vmcnt<(NS - 2) * 2 * LPW>();  // this wave's share of position J has landed
     __syncthreads();                   // ... and every other wave's
-    issue(slot_ref(SN{}), j + NS - 1);
-    if (live(j)) compute(slot_ref(S), j);
+    issue(slot_ref(SN{}), J + NS - 1);
+    if (live(J - base)) compute(slot_ref(S), J - base);
+  };
+  // Positions J0 .. J1-1 of one query tile; slots are (J - j_lo) mod NS, so a
+  // second tile (paired, NS = 2) may start on slot 1.
+  auto run = [&](int J0, int J1, int base) __attribute__((always_inline)) {
+    int J = J0;
+    if constexpr (NS == 2) {
+      if (((J - j_lo) & 1) && J < J1) {
+        step(std::integral_constant<int, 1>{}, J, base);
+        ++J;
+      }
+    }
+    for (; J < J1; J += NS) {
+      step(std::integral_constant<int, 0>{}, J, base);
+      if (J + 1 < J1) step(std::integral_constant<int, 1>{}, J + 1, base);
+      if constexpr (NS > 2) if (J + 2 < J1) step(std::integral_constant<int, 2>{}, J + 2, base);
+      if constexpr (NS > 3) if (J + 3 < J1) step(std::integral_constant<int, 3>{}, J + 3, base);
+    }
   };
 
   // Zero the ring once, so that rows a load leaves unwritten can never hold
@@ -398,33 +453,23 @@ void fwd_direct(FwdArgs a) {
   if constexpr (NS > 2) issue(ring1, j_lo + 1);
   if constexpr (NS > 3) issue(ring2, j_lo + 2);
 
-  for (int j0 = j_lo; j0 < nt; j0 += NS) {
-    step(std::integral_constant<int, 0>{}, j0);
-    if (j0 + 1 < nt) step(std::integral_constant<int, 1>{}, j0 + 1);
-    if constexpr (NS > 2) if (j0 + 2 < nt) step(std::integral_constant<int, 2>{}, j0 + 2);
-    if constexpr (NS > 3) if (j0 + 3 < nt) step(std::integral_constant<int, 3>{}, j0 + 3);
+  run(j_lo, nt0, 0);
+  if (pair) {
+    // the second query tile: its first keys are already in the ring; its Q
+    // loads land with them (the next step waits for both)
+    finish();
+    q0 = tl.t * kDirectBq;
+    qw0 = q0 + 32 * w;
+    qrow = qw0 + lr;
+    load_q();
+    m2 = -INFINITY;
+    lp = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = f32x16_t{};
+    run(nt0, nt, nt0);
   }
   wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
-
-  // Epilogue: O = o / l once per row; LSE = ln 2 * (m2 + log2 l).
-  const float lt = pair_sum(lp);
-  if (qrow < n && a.part_o) {
-    store_partial<NDB>(a, tl.bh, qrow, hl, o, m2, lt);
-  } else if (qrow < n) {
-    const float inv = a.o_mult / lt;
-    uint16_t* Og = (uint16_t*)hv.o + (size_t)qrow * hv.ors;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = db * 32 + 8 * g + 4 * hl;
-        const uint32_t x0 = pack2<IN>(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
-        const uint32_t x1 = pack2<IN>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-        *(u32x2_t*)(Og + d) = u32x2_t{x0, x1};
-      }
-    }
-    if (hl == 0 && hv.lse) hv.lse[qrow] = (m2 + __log2f(lt)) * kLn2;
-  }
+  finish();
 }
 
 // ---------------------------------------------------------------------------
@@ -914,6 +959,14 @@ hipError_t dispatch_causal(const FwdArgs& a, hipStream_t s) {
     return a.causal ? launch(fwd_direct8<D, true>, a, s, kDirectBq, kDirectThreads)
                     : launch(fwd_direct8<D, false>, a, s, kDirectBq, kDirectThreads);
   } else {
+    const int tiles = (a.n + kDirectBq - 1) / kDirectBq;
+    if (a.causal && !a.cu_seqlens && a.splits == 1 && tiles % 2 == 0 && FA_PAIR_TILES && FA_STAGES == 2) {
+      FwdArgs b = a;
+      b.pair = 1;
+      hipLaunchKernelGGL((fwd_direct<E, D, true>), dim3((unsigned)a.bh * (unsigned)(tiles / 2), 1u),
+                         dim3(kDirectThreads), 0, s, b);
+      return hipGetLastError();
+    }
     return a.causal ? launch(fwd_direct<E, D, true>, a, s, kDirectBq, kDirectThreads)
                     : launch(fwd_direct<E, D, false>, a, s, kDirectBq, kDirectThreads);
   }

@@ -42,6 +42,10 @@ struct FwdArgs {
   int split_keys;
   int splits;
   float* part_o;
+  // Causal f16 / bf16 launches with an even number of 256-row query tiles and
+  // no split or ragged batch: each workgroup takes tiles T-1-p and p of one
+  // head (set by the launcher).
+  int pair = 0;
   float* part_lse;
 };
 
