@@ -178,6 +178,12 @@ def time_steps(step, stream, steps, warmup):
     return evs[0].elapsed_time(evs[-1]) / steps, per
 
 
+def scrub_read(scrub, acc):
+    """Read every element of scrub (a sum into acc)."""
+    import torch
+    torch.sum(scrub, dim=0, out=acc)
+
+
 def cold_cache_pass(step, stream, flops, calls=10, scrub_bytes=512 << 20):
     """Per-call timing with scrub_bytes of device memory read before every
     call, so that no input is left in the L2s or the 256 MB Infinity Cache.
@@ -189,7 +195,7 @@ def cold_cache_pass(step, stream, flops, calls=10, scrub_bytes=512 << 20):
     acc = torch.zeros((), dtype=torch.float32, device="cuda")
     per = []
     for _ in range(calls):
-        torch.sum(scrub, dim=0, out=acc)
+        scrub_read(scrub, acc)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         step()
