@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -188,6 +189,9 @@ constexpr int kDirectBq = 32 * kDirectWaves;
 #ifndef FA_PAIR_TILES
 #define FA_PAIR_TILES 1
 #endif
+#ifndef FA_PAIR_TILES_NOMASK
+#define FA_PAIR_TILES_NOMASK 1
+#endif
 
 template <int D>
 struct DirectLayout {
@@ -230,7 +234,7 @@ void fwd_direct(FwdArgs a) {
   // the same head -- 2T + 2 key tiles in all, the same for every pair -- and
   // its K/V ring runs on from the first tile's keys into the second's, so
   // the second tile starts with its first keys already in LDS.
-  const bool pair = CAUSAL && a.pair;
+  const bool pair = a.pair;
   const TileId tl = pair ? tile_of_block(blockIdx.x, a.bh, tiles / 2, false, tiles)
                          : tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
   const HeadView hv = head_view<2, 2>(a, tl.bh);
@@ -951,6 +955,19 @@ hipError_t launch_combine_t(const CombineArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Compute units of the current device (256 on MI355X), read once per device.
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
+}
+
 template <Elt E, int D>
 hipError_t dispatch_causal(const FwdArgs& a, hipStream_t s) {
   if constexpr (E == Elt::F32) {
@@ -960,11 +977,18 @@ hipError_t dispatch_causal(const FwdArgs& a, hipStream_t s) {
                     : launch(fwd_direct8<D, false>, a, s, kDirectBq, kDirectThreads);
   } else {
     const int tiles = (a.n + kDirectBq - 1) / kDirectBq;
-    if (a.causal && !a.cu_seqlens && a.splits == 1 && tiles % 2 == 0 && FA_PAIR_TILES && FA_STAGES == 2) {
+    // Pairs of equal tiles (no mask) only when the paired grid still fills
+    // every CU; causal pairs are never longer than the longest unpaired tile.
+    const bool pair_ok = a.causal ? FA_PAIR_TILES
+                                  : FA_PAIR_TILES_NOMASK && (long)a.bh * (tiles / 2) >= device_cus();
+    if (!a.cu_seqlens && a.splits == 1 && tiles % 2 == 0 && pair_ok && FA_STAGES == 2) {
       FwdArgs b = a;
       b.pair = 1;
-      hipLaunchKernelGGL((fwd_direct<E, D, true>), dim3((unsigned)a.bh * (unsigned)(tiles / 2), 1u),
-                         dim3(kDirectThreads), 0, s, b);
+      const dim3 grid((unsigned)a.bh * (unsigned)(tiles / 2), 1u);
+      if (a.causal)
+        hipLaunchKernelGGL((fwd_direct<E, D, true>), grid, dim3(kDirectThreads), 0, s, b);
+      else
+        hipLaunchKernelGGL((fwd_direct<E, D, false>), grid, dim3(kDirectThreads), 0, s, b);
       return hipGetLastError();
     }
     return a.causal ? launch(fwd_direct<E, D, true>, a, s, kDirectBq, kDirectThreads)
