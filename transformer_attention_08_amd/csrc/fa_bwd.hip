@@ -33,6 +33,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -186,13 +187,19 @@ void bwd_dq(BwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 31, hl = lane >> 5;
   const int tiles = (a.n + kDqBq - 1) / kDqBq;
-  const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
+  // Paired query tiles, as in the forward: tile T-1-p, then tile p of the
+  // same head, with the K/V ring running on between them. The launcher pairs
+  // only when every first tile's key-tile count is a multiple of NS, so the
+  // second tile starts on slot 0.
+  const bool pair = a.pair;
+  const TileId tl = pair ? tile_of_block(blockIdx.x, a.bh, tiles / 2, false, tiles)
+                         : tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
   const BwdView hv = bwd_view(a, tl.bh);
   const int n = hv.n;
-  const int q0 = tl.t * kDqBq;
+  int q0 = (pair ? tiles - 1 - tl.t : tl.t) * kDqBq;
   if (q0 >= n) return;  // a tile past a short sequence (uniform)
-  const int qw0 = q0 + 32 * w;
-  const int qrow = qw0 + lr;
+  int qw0 = q0 + 32 * w;
+  int qrow = qw0 + lr;
   const uint32_t span = span_bytes(n, hv.rs, ROWB);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(hv.q, span);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(hv.k, span);
@@ -200,7 +207,9 @@ void bwd_dq(BwdArgs a) {
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(hv.o, span);
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(hv.g, span);
 
-  const int nt = ((CAUSAL ? min(q0 + kDqBq, n) : n) + BK - 1) / BK;  // key tiles 0 .. nt-1
+  // ring positions 0 .. nt-1: key tiles 0 .. nt0-1, then (paired) those of the second query tile
+  const int nt0 = ((CAUSAL ? min(q0 + kDqBq, n) : n) + BK - 1) / BK;
+  const int nt = pair ? nt0 + ((CAUSAL ? min(tl.t * kDqBq + kDqBq, n) : n) + BK - 1) / BK : nt0;
 
   uint32_t off[LPW];
 #pragma unroll
@@ -209,8 +218,9 @@ void bwd_dq(BwdArgs a) {
     const int row = byte / ROWB, p = (byte % ROWB) / 16;
     off[i] = (uint32_t)row * hv.rs + (uint32_t)((p ^ swz2<D>(row)) * 16);
   }
-  auto issue = [&](PairSlot<TILE_B>& slot, int t) __attribute__((always_inline)) {
-    const uint32_t base = t < nt ? (uint32_t)(t * BK) * hv.rs : 0x80000000u;
+  auto issue = [&](PairSlot<TILE_B>& slot, int J) __attribute__((always_inline)) {
+    const int t = pair && J >= nt0 ? J - nt0 : J;
+    const uint32_t base = J < nt ? (uint32_t)(t * BK) * hv.rs : 0x80000000u;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       lds_dma16(rk, slot.a + (w * LPW + i) * 1024, base + off[i]);
@@ -218,22 +228,27 @@ void bwd_dq(BwdArgs a) {
     }
   };
 
-  // Q and dO fragments (B operands), O only for D = rowsum(dO * O).
+  // Q and dO fragments (B operands), O only for D = rowsum(dO * O); D and
+  // -LSE log2(e) of this lane's row also go to the workspace.
   u32x4_t qf[NKS], gf[NKS];
-  float dpart = 0.f;
+  float dsum, nl2;
+  auto start_rows = [&]() __attribute__((always_inline)) {
+    float dpart = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    const uint32_t o_ = (uint32_t)qrow * hv.rs + (ks * 16 + hl * 8) * 2;
-    qf[ks] = bload16(rq, o_);
-    gf[ks] = bload16(rg, o_);
-    dpart += dot8<IN>(gf[ks], bload16(ro, o_));
-  }
-  const float dsum = pair_sum(dpart);
-  const float nl2 = qrow < n ? -hv.lse[qrow] * kLog2e : 0.f;
-  if (hl == 0 && qrow < n) {
-    hv.delta[qrow] = dsum;
-    hv.nlse2[qrow] = nl2;
-  }
+    for (int ks = 0; ks < NKS; ++ks) {
+      const uint32_t o_ = (uint32_t)qrow * hv.rs + (ks * 16 + hl * 8) * 2;
+      qf[ks] = bload16(rq, o_);
+      gf[ks] = bload16(rg, o_);
+      dpart += dot8<IN>(gf[ks], bload16(ro, o_));
+    }
+    dsum = pair_sum(dpart);
+    nl2 = qrow < n ? -hv.lse[qrow] * kLog2e : 0.f;
+    if (hl == 0 && qrow < n) {
+      hv.delta[qrow] = dsum;
+      hv.nlse2[qrow] = nl2;
+    }
+  };
+  start_rows();
   wait_vmcnt<0>();
 
   const int krow = perm32(lr);
@@ -247,8 +262,7 @@ void bwd_dq(BwdArgs a) {
   f32x16_t dq[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dq[db] = f32x16_t{};
-  const bool wave_live = qw0 < n;
-  auto live = [&](int j) __attribute__((always_inline)) { return wave_live && !(CAUSAL && j * BK > qw0 + 31); };
+  auto live = [&](int j) __attribute__((always_inline)) { return qw0 < n && !(CAUSAL && j * BK > qw0 + 31); };
   auto needs_mask = [&](int j) __attribute__((always_inline)) {
     return (j * BK + BK > n) || (CAUSAL && j * BK + BK - 1 > qw0);
   };
@@ -302,12 +316,21 @@ void bwd_dq(BwdArgs a) {
     else if constexpr (decltype(S)::value == 2) return ring2;
     else return ring3;
   };
-  auto step = [&](auto S, int j) __attribute__((always_inline)) {
+  auto step = [&](auto S, int J, int base) __attribute__((always_inline)) {
     using SN = std::integral_constant<int, (decltype(S)::value + NS - 1) % NS>;
     wait_vmcnt<(NS - 2) * 2 * LPW>();
     __syncthreads();
-    issue(slot_ref(SN{}), j + NS - 1);
-    if (live(j)) compute(slot_ref(S), j);
+    issue(slot_ref(SN{}), J + NS - 1);
+    if (live(J - base)) compute(slot_ref(S), J - base);
+  };
+  // positions J0 .. J1-1 (J0 a multiple of NS: slot J mod NS)
+  auto run = [&](int J0, int J1, int base) __attribute__((always_inline)) {
+    for (int J = J0; J < J1; J += NS) {
+      step(std::integral_constant<int, 0>{}, J, base);
+      if (J + 1 < J1) step(std::integral_constant<int, 1>{}, J + 1, base);
+      if constexpr (NS > 2) if (J + 2 < J1) step(std::integral_constant<int, 2>{}, J + 2, base);
+      if constexpr (NS > 3) if (J + 3 < J1) step(std::integral_constant<int, 3>{}, J + 3, base);
+    }
   };
 
   {
@@ -323,11 +346,16 @@ void bwd_dq(BwdArgs a) {
   issue(ring0, 0);
   if constexpr (NS > 2) issue(ring1, 1);
   if constexpr (NS > 3) issue(ring2, 2);
-  for (int j0 = 0; j0 < nt; j0 += NS) {
-    step(std::integral_constant<int, 0>{}, j0);
-    if (j0 + 1 < nt) step(std::integral_constant<int, 1>{}, j0 + 1);
-    if constexpr (NS > 2) if (j0 + 2 < nt) step(std::integral_constant<int, 2>{}, j0 + 2);
-    if constexpr (NS > 3) if (j0 + 3 < nt) step(std::integral_constant<int, 3>{}, j0 + 3);
+  run(0, nt0, 0);
+  if (pair) {
+    if (qrow < n) store_rows<IN, NDB>((uint16_t*)hv.dq + (size_t)qrow * (hv.rs / 2), hl, dq, a.scale);
+    q0 = tl.t * kDqBq;
+    qw0 = q0 + 32 * w;
+    qrow = qw0 + lr;
+    start_rows();
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dq[db] = f32x16_t{};
+    run(nt0, nt, nt0);
   }
   wait_vmcnt<0>();
 
@@ -548,17 +576,41 @@ void bwd_dkdv(BwdArgs a) {
   }
 }
 
+#ifndef FA_BWD_PAIR
+#define FA_BWD_PAIR 1
+#endif
+
+// Compute units of the current device, read once per device.
+int bwd_device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
+}
+
 template <Elt E, int D>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
-  const unsigned g1 = (unsigned)a.bh * (unsigned)((a.n + kDqBq - 1) / kDqBq);
+  const int tiles = (a.n + kDqBq - 1) / kDqBq;
+  // Paired dQ tiles when every first tile ends on a full ring round (n a
+  // multiple of the tile, NS dividing the key tiles per query tile) and, without
+  // a mask, while the paired grid still covers every CU.
+  BwdArgs b = a;
+  b.pair = !a.cu_seqlens && tiles % 2 == 0 && a.n % kDqBq == 0 && (kDqBq / FA_BWD_TILE) % kBwdStages == 0 &&
+           FA_BWD_PAIR && (a.causal || (long)a.bh * (tiles / 2) >= bwd_device_cus());
+  const unsigned g1 = (unsigned)a.bh * (unsigned)(b.pair ? tiles / 2 : tiles);
   const unsigned g2 = (unsigned)a.bh * (unsigned)((a.n + kKvBk - 1) / kKvBk);
   if (a.causal) {
-    hipLaunchKernelGGL((bwd_dq<E, D, true>), dim3(g1), dim3(kDqThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_dq<E, D, true>), dim3(g1), dim3(kDqThreads), 0, s, b);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv<E, D, true>), dim3(g2), dim3(kKvThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL((bwd_dq<E, D, false>), dim3(g1), dim3(kDqThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_dq<E, D, false>), dim3(g1), dim3(kDqThreads), 0, s, b);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv<E, D, false>), dim3(g2), dim3(kKvThreads), 0, s, a);

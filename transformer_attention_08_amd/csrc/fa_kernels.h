@@ -91,6 +91,8 @@ struct BwdArgs {
   float c;            // scale * log2(e)
   float scale;
   Elt elt;            // F16 or BF16
+  // Paired query tiles in the dQ pass (as FwdArgs::pair; set by the launcher).
+  int pair = 0;
 };
 
 // Unfused forward (f16 / bf16): S and P materialised in the caller's
