@@ -167,3 +167,30 @@ def test_llama_shape_sampled_rows_and_keys():
                                                      cols, lse_h, dsum_h)
         compare([dq_c[0, hh][rows], dk_c[0, hh][cols], dv_c[0, hh][cols]], [ref_dq, ref_dk, ref_dv],
                 "bf16", f"head {hh}")
+
+
+def test_paired_dq_tiles_without_mask():
+    """32 heads, n = 4096, d_k 64, no mask: the dQ pass pairs query tiles
+    (32 x 16 / 2 = 256 workgroups); sampled dQ rows and dK / dV key columns of
+    two heads against the oracle."""
+    b, h, n, d = 1, 32, 4096, 64
+    say("backward, paired dQ tiles, no mask")
+    inp, do = workload.make_inputs_with_grad(b, h, n, d, "bf16", seed=13)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    dev = inp.to("cuda")
+    o, lse = fa.forward(dev.q, dev.k, dev.v, causal=False, scale=scale)
+    dq, dk, dv = fa.backward(dev.q, dev.k, dev.v, o, lse, do.cuda(), causal=False, scale=scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(13)
+    rows = np.unique(np.concatenate([[0, 255, 256, 2047, 2048, n - 1], rng.integers(0, n, 40)]))
+    cols = np.unique(np.concatenate([[0, 127, n - 1], rng.integers(0, n, 40)]))
+    dq_c, dk_c, dv_c = (decode(t.cpu(), "bf16") for t in (dq, dk, dv))
+    q, k, v = oracle_inputs(inp)
+    g = decode(do, "bf16")
+    for hh in (0, 17):
+        ref_dq, _ = oracle.backward_rows(q[0, hh], k[0, hh], v[0, hh], g[0, hh], scale, False, rows)
+        lse_h, dsum_h = oracle.head_statistics(q[0, hh], k[0, hh], v[0, hh], g[0, hh], scale, False)
+        ref_dk, ref_dv = oracle.backward_key_columns(q[0, hh], k[0, hh], v[0, hh], g[0, hh], scale, False,
+                                                     cols, lse_h, dsum_h)
+        compare([dq_c[0, hh][rows], dk_c[0, hh][cols], dv_c[0, hh][cols]], [ref_dq, ref_dk, ref_dv],
+                "bf16", f"head {hh}")

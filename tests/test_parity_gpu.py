@@ -82,6 +82,31 @@ def test_workload_sampled_rows(name, seed):
     check(workload.workload_inputs(w, seed), w.causal, w.scale, rows=rows)
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64)])
+def test_paired_tiles_without_mask(dtype, d):
+    """32 heads, n = 4096, no mask: 32 x 16 / 2 = 256 paired workgroups fill
+    the CUs, so the launcher pairs query tiles 15-p and p (the path the
+    sampled workloads above, all causal or e4m3, do not take); rows of both
+    tiles of every pair, and every head, against the oracle."""
+    b, h, n = 1, 32, 4096
+    say(f"paired, no mask: [{b}, {h}, {n}, {d}] {dtype}")
+    inp = workload.make_inputs(b, h, n, d, dtype, seed=11)
+    rows = workload.sample_rows(n, 384, seed=11)
+    check(inp, False, float(np.float32(1 / math.sqrt(d))), rows=rows)
+
+
+@pytest.mark.parametrize("n", [8000, 2000])
+def test_paired_causal_tiles_with_ragged_tail(n):
+    """Causal with an even tile count but n not a multiple of 256: the first
+    tile of pair 0 is the ragged last tile, so the second tile of that pair
+    starts on the other ring slot."""
+    b, h, d = 1, 8, 128
+    say(f"paired causal, ragged tail: n = {n}")
+    inp = workload.make_inputs(b, h, n, d, "bf16", seed=12)
+    rows = workload.sample_rows(n, 384, seed=12)
+    check(inp, True, float(np.float32(1 / math.sqrt(d))), rows=rows)
+
+
 # ------------------------------------------------------------ invariants
 
 def _dev(t):
