@@ -32,10 +32,13 @@
 // base-2 units; LSE is converted back to natural-log units at the end.
 //
 // Work decomposition. The grid has one workgroup per (batch*head, query
-// tile). Causal launches visit the longest query tiles first. When the
-// number of (batch, head) pairs is a multiple of 8, the workgroups of each
-// head are mapped onto one XCD (workgroups are dispatched round-robin over
-// the 8 XCDs), so the K/V tiles of a head are re-read from that XCD's L2.
+// tile), or, for the f16 / bf16 kernel with an even tile count, one per pair
+// of query tiles T-1-p and p of a head (equal work under a causal mask; the
+// K/V ring runs on from one tile into the other). Unpaired causal launches
+// visit the longest query tiles first. When the number of (batch, head)
+// pairs is a multiple of 8, the workgroups of each head are mapped onto one
+// XCD (workgroups are dispatched round-robin over the 8 XCDs), so the K/V
+// tiles of a head are re-read from that XCD's L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
