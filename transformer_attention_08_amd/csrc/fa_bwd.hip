@@ -470,18 +470,31 @@ void bwd_dkdv(BwdArgs a) {
     return (kw0 + 31 >= n) || (CAUSAL && i * kKvBq < kw0 + 31);
   };
 
+  // S = Q K^T and dP = dO V^T of the 32-query block qb
+  auto sdp = [&](const QSlot<TILE_B>& slot, int qb, f32x16_t& s, f32x16_t& dp) __attribute__((always_inline)) {
+    s = f32x16_t{};
+    dp = f32x16_t{};
+    const int row = qb * 32 + qr;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int at = row * ROWB + (((2 * ks + hl) ^ sw_r) * 16);
+      s = mfma16<IN>(*(const u32x4_t*)(slot.q + at), kf[ks], s);
+      dp = mfma16<IN>(*(const u32x4_t*)(slot.g + at), vf[ks], dp);
+    }
+  };
+  // Per tile, the products of block qb + 1 are issued before the softmax of
+  // block qb, so that a wave (alone on its SIMD) has them on the matrix pipe
+  // while it works on the exponentials.
   auto compute = [&](const QSlot<TILE_B>& slot, int it) __attribute__((always_inline)) {
+    constexpr int QB = kKvBq / 32;
     const bool mask = needs_mask(it);
+    f32x16_t s[2], dp[2];
+    sdp(slot, 0, s[0], dp[0]);
 #pragma unroll
-    for (int qb = 0; qb < kKvBq / 32; ++qb) {
-      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-      const int row = qb * 32 + qr;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int at = row * ROWB + (((2 * ks + hl) ^ sw_r) * 16);
-        s = mfma16<IN>(*(const u32x4_t*)(slot.q + at), kf[ks], s);
-        dp = mfma16<IN>(*(const u32x4_t*)(slot.g + at), vf[ks], dp);
-      }
+    for (int qb = 0; qb < QB; ++qb) {
+      if (qb + 1 < QB) sdp(slot, qb + 1, s[(qb + 1) & 1], dp[(qb + 1) & 1]);
+      f32x16_t& sc = s[qb & 1];
+      const f32x16_t& dc = dp[qb & 1];
       // register i holds query qb*32 + 8*hl + i (i < 8) or qb*32 + 16 + 8*hl + i - 8
       float nl[16], dd[16];
 #pragma unroll
@@ -503,16 +516,16 @@ void bwd_dkdv(BwdArgs a) {
         for (int r = 0; r < 16; ++r) {
           const int q_ = it * kKvBq + qb * 32 + 16 * (r >> 3) + 8 * hl + (r & 7);
           const bool ok = key < n && (!CAUSAL || key <= q_);
-          s[r] = ok ? s[r] : -INFINITY;
+          sc[r] = ok ? sc[r] : -INFINITY;
         }
       }
       u32x4_t pb[2], dsb[2];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(s[r], c, nl[r]));
-        const float p1 = fast_exp2(__builtin_fmaf(s[r + 1], c, nl[r + 1]));
+        const float p0 = fast_exp2(__builtin_fmaf(sc[r], c, nl[r]));
+        const float p1 = fast_exp2(__builtin_fmaf(sc[r + 1], c, nl[r + 1]));
         pb[r >> 3][(r & 7) >> 1] = pack2<IN>(p0, p1);
-        dsb[r >> 3][(r & 7) >> 1] = pack2<IN>(p0 * (dp[r] - dd[r]), p1 * (dp[r + 1] - dd[r + 1]));
+        dsb[r >> 3][(r & 7) >> 1] = pack2<IN>(p0 * (dc[r] - dd[r]), p1 * (dc[r + 1] - dd[r + 1]));
       }
       // dV^T += dO^T P,  dK^T += Q^T dS
 #pragma unroll
