@@ -38,7 +38,8 @@
  * or host memory per call and no n x n buffer; the entry points that need
  * scratch memory (fa_forward_splitkv, fa_backward) take it from the caller
  * as a workspace argument. It holds no state beyond per-process kernel
- * registration. Inputs are only read. Outputs are written in full (every
+ * registration and each device's compute-unit count, read once (it decides
+ * how query tiles are grouped into workgroups). Inputs are only read. Outputs are written in full (every
  * element of the valid rows) and must not overlap the inputs or each other.
  * Calls are reentrant and thread-safe.
  *
