@@ -308,7 +308,7 @@ void fwd_direct(FwdArgs a) {
   auto live = [&](int j) __attribute__((always_inline)) { return qw0 < n && !(CAUSAL && j * BK > qw0 + 31); };
   auto needs_mask = [&](int j) __attribute__((always_inline)) { return (j * BK + BK > n) || (CAUSAL && j * BK + BK - 1 > qw0); };
 
-  auto compute = [&](const LdsSlot<TILE_B>& slot, int j) __attribute__((always_inline)) {
+  auto compute = [&](const LdsSlot<TILE_B>& slot, int j, auto&& mid) __attribute__((always_inline)) {
     // S^T = K Q^T
     f32x16_t s[KB];
 #pragma unroll
@@ -368,6 +368,8 @@ void fwd_direct(FwdArgs a) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[db] *= alpha;
     }
+    // the next tile's copies go out here, between the softmax and P.V (see step)
+    mid();
     // O^T += V^T P^T; consecutive MFMAs go to different accumulators
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -421,8 +423,12 @@ void fwd_direct(FwdArgs a) {
     using SN = std::integral_constant<int, (decltype(S)::value + NS - 1) % NS>;
     wait_vmcnt<(NS - 2) * 2 * LPW>();  // this wave's share of position J has landed
     __syncthreads();                   // ... and every other wave's
-    issue(slot_ref(SN{}), J + NS - 1);
-    if (live(J - base)) compute(slot_ref(S), J - base);
+    // The copies of position J + NS - 1 are issued inside the compute, after
+    // the softmax and before P.V: their LDS writes then overlap the P.V
+    // phase rather than Q K^T (measured +1.5% over issuing them first).
+    auto refill = [&]() __attribute__((always_inline)) { issue(slot_ref(SN{}), J + NS - 1); };
+    if (live(J - base)) compute(slot_ref(S), J - base, refill);
+    else refill();
   };
   // Positions J0 .. J1-1 of one query tile; slots are (J - j_lo) mod NS, so a
   // second tile (paired, NS = 2) may start on slot 1.
