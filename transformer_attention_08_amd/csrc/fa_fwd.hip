@@ -192,9 +192,46 @@ constexpr int kDirectBq = 32 * kDirectWaves;
 #ifndef FA_PAIR_TILES
 #define FA_PAIR_TILES 1
 #endif
+#ifndef FA_QK_AHEAD
+#define FA_QK_AHEAD 6
+#endif
 #ifndef FA_PAIR_TILES_NOMASK
 #define FA_PAIR_TILES_NOMASK 1
 #endif
+
+// S^T = K Q^T for one key tile: KB accumulators of 32 keys, NKS k-steps.
+// K is read from its swizzled LDS tile (row kb * 32 + krow, 16-byte chunk
+// 2 ks + hl of the row, XOR kswz); Q is the register-held B operand. With
+// FA_QK_AHEAD > 0 the K operands are read that many MFMAs ahead in a fixed
+// order (operand i, i.e. k-step i / KB of key block i % KB, feeds MFMA i, and
+// the read of operand i + FA_QK_AHEAD goes out right after MFMA i), so that
+// LDS latency hides behind the MFMAs already issued.
+template <Elt IN, int KB, int NKS, int ROWB>
+__device__ inline void qk_tile(f32x16_t (&s)[KB], const uint8_t* k, int krow, int kswz, int hl,
+                               const u32x4_t (&qf)[NKS]) {
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16_t{};
+  auto kaddr = [&](int i) __attribute__((always_inline)) {
+    const int ks = i / KB, kb = i % KB;
+    return (const u32x4_t*)(k + (kb * 32 + krow) * ROWB + (((2 * ks + hl) ^ kswz) * 16));
+  };
+#if FA_QK_AHEAD > 0
+  constexpr int NQ = NKS * KB, PA = FA_QK_AHEAD < NQ ? FA_QK_AHEAD : NQ;
+  u32x4_t kf[PA];
+#pragma unroll
+  for (int i = 0; i < PA; ++i) kf[i] = *kaddr(i);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    s[i % KB] = mfma16<IN>(kf[i % PA], qf[i / KB], s[i % KB]);
+    if (i + PA < NQ) kf[i % PA] = *kaddr(i + PA);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#else
+#pragma unroll
+  for (int i = 0; i < NKS * KB; ++i) s[i % KB] = mfma16<IN>(*kaddr(i), qf[i / KB], s[i % KB]);
+#endif
+}
 
 template <int D>
 struct DirectLayout {
@@ -311,17 +348,7 @@ void fwd_direct(FwdArgs a) {
   auto compute = [&](const LdsSlot<TILE_B>& slot, int j, auto&& mid) __attribute__((always_inline)) {
     // S^T = K Q^T
     f32x16_t s[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16_t{};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const u32x4_t av = *(const u32x4_t*)(slot.k + (kb * 32 + krow) * ROWB +
-                                             (((2 * ks + hl) ^ kswz) * 16));
-        s[kb] = mfma16<IN>(av, qf[ks], s[kb]);
-      }
-    }
+    qk_tile<IN, KB, NKS, ROWB>(s, slot.k, krow, kswz, hl, qf);
     if (needs_mask(j)) {
       const int kbase = j * BK;
 #pragma unroll
@@ -601,16 +628,7 @@ void fwd_direct8(FwdArgs a) {
   // the compute of fwd_direct on the widened tile
   auto compute = [&](const LdsSlot<TILE_B>& slot, int j) __attribute__((always_inline)) {
     f32x16_t s[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16_t{};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const u32x4_t av = *(const u32x4_t*)(slot.k + (kb * 32 + krow) * ROWB + (((2 * ks + hl) ^ kswz) * 16));
-        s[kb] = mfma16<Elt::BF16>(av, qf[ks], s[kb]);
-      }
-    }
+    qk_tile<Elt::BF16, KB, NKS, ROWB>(s, slot.k, krow, kswz, hl, qf);
     if (needs_mask(j)) {
       const int kbase = j * BK;
 #pragma unroll
