@@ -309,3 +309,20 @@ def test_backward_varlen_validation(lib):
     assert bvcall(lib, total=0) == 0   # no rows: returns before any HIP call
     if torch.cuda.device_count() == 0:
         assert bvcall(lib) == 9
+
+
+def test_library_imports_no_allocator():
+    """The library allocates no device or host memory: its dynamic imports
+    hold no allocation or free routine of the HIP runtime, so no n x n score
+    buffer (128 GiB in fp32 at 32 heads, n = 32768) can exist on any path."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm is not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", fa.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    imports = {line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()}
+    assert "hipLaunchKernel" in imports  # the symbol table was read
+    alloc = sorted(s for s in imports if re.search(r"(Malloc|Alloc|Free|MemPool|hipMemCreate|HostRegister)", s))
+    assert alloc == [], alloc

@@ -230,3 +230,32 @@ def test_errors_surface_from_binding():
     with pytest.raises(fa.FAError) as e:
         fa.forward(x, x, x)
     assert e.value.status == 4
+
+
+def test_long_context_allocates_nothing():
+    """The long-context shape [1, 32, 32768, 128] bf16 causal runs in the
+    memory of its inputs and outputs: free device memory is the same before
+    and after the call (outputs passed in), at n = 8192 and at n = 32768, so
+    memory grows with n as Q, K, V, O and LSE do, linearly; an fp32 score
+    matrix alone would need 128 GiB at n = 32768."""
+    import transformer_attention_08_amd as fa
+    b, h, d = 1, 32, 128
+    warm = torch.randn(1, 8, 512, d, device="cuda").to(torch.bfloat16)
+    fa.forward(warm, warm, warm, causal=True)  # the kernel's code object is loaded
+    torch.cuda.synchronize()
+    used = {}
+    for n in (8192, 32768):
+        say(f"memory at n = {n}")
+        q, k, v = (torch.randn(b, h, n, d, device="cuda").to(torch.bfloat16) for _ in range(3))
+        out = torch.empty_like(q)
+        lse = torch.empty(b, h, n, device="cuda")
+        torch.cuda.synchronize()
+        free0, _ = torch.cuda.mem_get_info()
+        fa.forward(q, k, v, causal=True, out=out, lse=lse)
+        torch.cuda.synchronize()
+        free1, _ = torch.cuda.mem_get_info()
+        assert free0 - free1 <= 2 << 20, (n, free0 - free1)
+        used[n] = sum(t.numel() * t.element_size() for t in (q, k, v, out, lse))
+        assert torch.isfinite(out[0, :, -1].float()).all()
+        del q, k, v, out, lse
+    assert used[32768] == 4 * used[8192]
