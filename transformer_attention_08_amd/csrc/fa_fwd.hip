@@ -23,8 +23,9 @@
 //     and 3 of the row index swapped) so that the 8 keys a lane feeds into
 //     one P.V MFMA step are 8 consecutive keys. A sum over keys does not
 //     depend on their order, so only the K and V tile reads need to agree.
-// V is transposed once per tile while it is written to LDS, so that the A
-// operand of O^T = V^T P^T is one 16-byte LDS read per lane.
+// V rows keep their memory order in LDS; the A operand of O^T = V^T P^T
+// (eight consecutive keys at one d-column per lane) comes from two
+// transposing LDS reads (ds_read_b64_tr_b16) of four keys each.
 //
 // Scale. The exponentials are exp2 with c = scale * log2(e) folded into the
 // score ("Mastering FlashAttention: The Algebraic Foundation", key points:
