@@ -333,7 +333,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="llama3_8b_bf16_causal")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--splits", type=int, default=1,
-                    help="cut the keys into this many blocks (fa_forward_splitkv) and merge")
+                    help="cut the keys into this many blocks (fa_forward_splitkv) and merge; "
+                         "0: the count fa_splitkv_splits chooses for the device")
     ap.add_argument("--backward", action="store_true",
                     help="time fa_backward (dQ, dK, dV) instead of the forward")
     ap.add_argument("--unfused", action="store_true",
@@ -380,6 +381,8 @@ def main(argv=None):
     d = inp.to(dev)
     o = torch.empty(w.batch, w.heads, w.n, w.d_k, dtype=workload.torch_dtype(w.out_dtype), device=dev)
     lse = torch.empty(w.batch, w.heads, w.n, dtype=torch.float32, device=dev)
+    if args.splits == 0:
+        args.splits = fa.splitkv_splits(w.batch, w.heads, w.n, w.causal)
     if args.splits > 1 and w.dtype == "fp8" and (inp.q_descale, inp.k_descale, inp.v_descale) != (1, 1, 1):
         print("the split-KV entry takes e4m3 with unit descales only", file=sys.stderr)
         return 2

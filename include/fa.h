@@ -192,6 +192,23 @@ int fa_forward_splitkv(const void* q, const void* k, const void* v, void* o, flo
 size_t fa_splitkv_workspace_size(int batch, int heads, int n, int d_k, int splits);
 
 /*
+ * fa_splitkv_splits -- a key-block count for fa_forward_splitkv. Splitting
+ * pays only while the (batch, head, 256-row query tile) units leave compute
+ * units idle; under a causal mask the longest tiles set the time, so twice
+ * as many units are asked for. The count doubles from 1 while
+ *     batch * heads * ceil(n / 256) * splits < compute_units * (causal ? 2 : 1)
+ * and every block would still hold at least 256 keys (512 * splits <= n),
+ * up to 256. Examples with 256 compute units: 2 heads, n = 4096, no mask ->
+ * 8; 4 heads, n = 16384, causal -> 2; 64 (batch, head) pairs, n = 2048,
+ * causal -> 1 (these are the measured best choices).
+ *   compute_units  the device's compute-unit count; <= 0 reads it from the
+ *                  current HIP device (256 when that query fails).
+ * Returns 0 for invalid sizes (batch, heads or n < 1, causal not 0 or 1).
+ * Host code only; the query of the device is its only HIP call.
+ */
+int fa_splitkv_splits(int batch, int heads, int n, int causal, int compute_units);
+
+/*
  * fa_backward -- gradients of the attention of fa_forward (f16 / bf16).
  *
  * Given dO = dL/dO of a scalar loss L, with P = softmax_rows(scale Q K^T +

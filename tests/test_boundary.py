@@ -326,3 +326,24 @@ def test_library_imports_no_allocator():
     assert "hipLaunchKernel" in imports  # the symbol table was read
     alloc = sorted(s for s in imports if re.search(r"(Malloc|Alloc|Free|MemPool|hipMemCreate|HostRegister)", s))
     assert alloc == [], alloc
+
+
+@pytest.mark.parametrize("args,want", [
+    ((1, 2, 4096, 0, 256), 8),       # two heads, no mask: 32 units -> 256
+    ((1, 4, 16384, 1, 256), 2),      # causal asks for twice the compute units
+    ((2, 32, 2048, 1, 256), 1),      # grid already full
+    ((1, 32, 8192, 1, 256), 1),
+    ((1, 1, 256, 0, 256), 1),        # blocks would hold fewer than 256 keys
+    ((1, 1, 1 << 20, 0, 1 << 20), 256),  # capped at 256 blocks
+    ((1, 1, 4096, 0, 304), 16),      # 16 units; blocks of 256 keys are the floor
+    ((0, 1, 10, 0, 256), 0), ((1, 0, 10, 0, 256), 0), ((1, 1, 0, 0, 256), 0), ((1, 1, 10, 2, 256), 0),
+])
+def test_splitkv_split_count_rule(lib, args, want):
+    assert lib.fa_splitkv_splits(*args) == want
+
+
+def test_splitkv_split_count_queries_the_device(lib):
+    # without a GPU the device query fails and 256 compute units are assumed;
+    # with one, the device's own count is used
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count if torch.cuda.is_available() else 256
+    assert lib.fa_splitkv_splits(1, 2, 4096, 0, 0) == lib.fa_splitkv_splits(1, 2, 4096, 0, n_cus)

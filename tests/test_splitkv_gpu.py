@@ -137,3 +137,27 @@ def test_long_rows_sampled():
                lse_ref, "bf16")
     say("   ", r)
     assert r["lse_max"] <= LSE_TOL and r["o_max"] <= O_TOL["bf16"], r
+
+
+def test_chosen_split_count_on_two_heads():
+    """splits=None takes fa_splitkv_splits' count for the device (8 for two
+    heads of 4096 keys on 256 compute units); the merged result meets the
+    oracle on sampled rows of both heads."""
+    b, h, n, d = 1, 2, 4096, 128
+    chosen = fa.splitkv_splits(b, h, n, False)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert chosen == fa.splitkv_splits(b, h, n, False, cus)
+    say(f"splitkv chosen splits={chosen} on {cus} compute units")
+    assert chosen > 1
+    inp = workload.make_inputs(b, h, n, d, "bf16", seed=21)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    dv = inp.to("cuda")
+    o, lse, ws = fa.forward_splitkv(dv.q, dv.k, dv.v, None, causal=False, scale=scale)
+    torch.cuda.synchronize()
+    assert ws.numel() == fa.splitkv_workspace_size(b, h, n, d, chosen)
+    rows = workload.sample_rows(n, 256, 21)
+    o_ref, lse_ref = oracle_forward(inp, False, scale, rows=rows)
+    r = report(o.cpu().double().numpy()[:, :, rows], lse.cpu().double().numpy()[:, :, rows], o_ref,
+               lse_ref, "bf16")
+    say("   ", r)
+    assert r["lse_max"] <= LSE_TOL and r["o_max"] <= O_TOL["bf16"], r

@@ -34,7 +34,7 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_DTYPE",
           8: "FA_ERR_OVERFLOW", 9: "FA_ERR_HIP"}
 
 EXPORTS = ("fa_forward", "fa_forward_fp8", "fa_forward_strided", "fa_forward_varlen",
-           "fa_forward_splitkv", "fa_splitkv_workspace_size",
+           "fa_forward_splitkv", "fa_splitkv_workspace_size", "fa_splitkv_splits",
            "fa_backward", "fa_backward_workspace_size", "fa_backward_varlen", "fa_forward_unfused",
            "fa_unfused_workspace_size", "fa_status_string", "fa_last_hip_error",
            "fa_abi_version")
@@ -67,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_forward_splitkv.restype = i
     lib.fa_splitkv_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_splitkv_workspace_size.restype = sz
+    lib.fa_splitkv_splits.argtypes = [i, i, i, i, i]
+    lib.fa_splitkv_splits.restype = i
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp]
     lib.fa_backward.restype = i
     lib.fa_backward_workspace_size.argtypes = [i, i, i]
@@ -176,17 +178,25 @@ def splitkv_workspace_size(batch: int, heads: int, n: int, d_k: int, splits: int
     return int(load_library().fa_splitkv_workspace_size(batch, heads, n, d_k, splits))
 
 
-def forward_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, splits: int,
+def splitkv_splits(batch: int, heads: int, n: int, causal: bool, compute_units: int = 0) -> int:
+    """``fa_splitkv_splits``: the library's key-block count for these sizes
+    (compute_units <= 0: the current device's)."""
+    return int(load_library().fa_splitkv_splits(batch, heads, n, 1 if causal else 0, int(compute_units)))
+
+
+def forward_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, splits: Optional[int] = None,
                     causal: bool = False, scale: Optional[float] = None,
                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None):
-    """``fa_forward_splitkv``: keys cut into ``splits`` blocks, partial results
-    merged by their log-sum-exp. Returns (O, LSE, workspace); the workspace
-    (uint8 device tensor, allocated here unless given) holds the per-block
-    partials after the call."""
+    """``fa_forward_splitkv``: keys cut into ``splits`` blocks (None: the count
+    ``fa_splitkv_splits`` gives), partial results merged by their log-sum-exp.
+    Returns (O, LSE, workspace); the workspace (uint8 device tensor, allocated
+    here unless given) holds the per-block partials after the call."""
     lib = load_library()
     out, lse = _prepare(q, k, v, out, lse)
     b, h, n, d = q.shape
+    if splits is None:
+        splits = splitkv_splits(b, h, n, causal)
     need = splitkv_workspace_size(b, h, n, d, splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)

@@ -419,6 +419,24 @@ size_t fa_splitkv_workspace_size(int batch, int heads, int n, int d_k, int split
   return split_layout(batch, heads, n, d_k, used).total;
 }
 
+int fa_splitkv_splits(int batch, int heads, int n, int causal, int compute_units) {
+  if (batch < 1 || heads < 1 || n < 1 || (causal != 0 && causal != 1)) return 0;
+  int cus = compute_units;
+  if (cus <= 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+      (void)hipGetLastError();  // leave no error behind for a later launch check
+      cus = 256;
+    }
+  }
+  const int64_t units = (int64_t)batch * heads * ((n + 255) / 256);
+  const int64_t want = (int64_t)cus * (causal ? 2 : 1);
+  int splits = 1;
+  while (units * splits < want && 2 * splits <= kMaxSplits && (int64_t)512 * splits <= n) splits *= 2;
+  return splits;
+}
+
 int fa_forward_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
                        int heads, int n, int d_k, float scale, int causal, int dtype, int splits,
                        void* workspace, size_t workspace_bytes, void* stream) {
