@@ -1,0 +1,63 @@
+"""The entry points under HIP graph capture: fa_forward and
+fa_forward_splitkv allocate nothing and only enqueue kernels on the caller's
+stream, so a captured call replays. Each replay runs after eager work that
+overwrites the outputs, and must reproduce the eager result bit for bit."""
+import pytest
+import torch
+
+import transformer_attention_08_amd as fa
+import workload
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _capture(fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()  # warm-up outside the graph (kernel code objects loaded)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_replays(causal):
+    say(f"graph replay, fa_forward causal={causal}")
+    d = workload.make_inputs(1, 8, 1000, 128, "bf16", seed=31).to("cuda")
+    o_ref, lse_ref = fa.forward(d.q, d.k, d.v, causal=causal)
+    out, lse = torch.empty_like(o_ref), torch.empty_like(lse_ref)
+    g = _capture(lambda: fa.forward(d.q, d.k, d.v, causal=causal, out=out, lse=lse))
+    for rep in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_ref) and torch.equal(lse, lse_ref), rep
+
+
+def test_splitkv_replays():
+    say("graph replay, fa_forward_splitkv (blocks + merge)")
+    d = workload.make_inputs(1, 2, 2048, 128, "bf16", seed=32).to("cuda")
+    splits = 4
+    o_ref, lse_ref, _ = fa.forward_splitkv(d.q, d.k, d.v, splits)
+    out, lse = torch.empty_like(o_ref), torch.empty_like(lse_ref)
+    ws = torch.empty(fa.splitkv_workspace_size(1, 2, 2048, 128, splits), dtype=torch.uint8, device="cuda")
+    g = _capture(lambda: fa.forward_splitkv(d.q, d.k, d.v, splits, out=out, lse=lse, workspace=ws))
+    for rep in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        ws.fill_(255)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_ref) and torch.equal(lse, lse_ref), rep
