@@ -37,9 +37,9 @@ struct TileId {
 // one sequence of a ragged batch -- spread over all XCDs. Each XCD takes its
 // heads in groups of G, the longest tiles of a group first: a head's
 // workgroups then run close together and re-read its K/V tiles from L2
-// rather than HBM. Heads of 128 tiles or more go one at a time (a head's
+// rather than HBM. Heads of 64 tiles or more go one at a time (a head's
 // keys then stream through the XCD in fewer rounds of its CUs), heads of 32
-// to 127 tiles in groups of 2; short ones in one group, where the longest
+// to 63 tiles in groups of 2; short ones in one group, where the longest
 // tiles of every head going first matters more for the tail than the
 // re-reads. head_tiles (when not negative) is the
 // head's length in tiles for that choice, when a workgroup holds more than
@@ -49,7 +49,7 @@ __device__ inline TileId tile_of_block(int pid, int bh_count, int tiles, bool re
   if ((bh_count & 7) == 0) {
     const int xcd = pid & 7, slot = pid >> 3, per = bh_count >> 3;
     const int ht = head_tiles < 0 ? tiles : head_tiles;
-    const int G = ht >= 128 ? 1 : (ht >= 32 && (per & 1) == 0) ? 2 : per;
+    const int G = ht >= 64 ? 1 : (ht >= 32 && (per & 1) == 0) ? 2 : per;
     const int g = slot / (G * tiles), r = slot - g * (G * tiles);
     tt = r / G;
     bh = (g * G + r % G) * 8 + xcd;
