@@ -31,8 +31,11 @@
  *
  * Supported shapes. batch, heads >= 1; n >= 1 (any n: ragged tails are
  * masked inside the kernel); d_k in {64, 128}; causal in {0, 1}; scale
- * finite and >= 0 (the method's scale is 1/sqrt(d_k); the library folds
- * log2(e) into it and evaluates exponentials as exp2).
+ * any finite value whose product with log2(e) is finite (the method's scale
+ * is 1/sqrt(d_k); the equation admits any scalar). The library folds log2(e)
+ * into |scale| and evaluates exponentials as exp2; a negative scale is
+ * applied by negating q inside the kernel, which is exact:
+ * scale (q . k) = |scale| ((-q) . k).
  *
  * Ownership. The caller owns every buffer. The library allocates no device
  * or host memory per call and no n x n buffer; the entry points that need
@@ -78,7 +81,8 @@ typedef enum {
   FA_ERR_UNSUPPORTED = 4, /* d_k not in {64, 128}, causal not in {0, 1}, or a mode  */
                           /* this entry point does not offer                       */
   FA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                       */
-  FA_ERR_SCALE = 6,       /* scale (or a descale) is not finite, or is negative     */
+  FA_ERR_SCALE = 6,       /* scale not finite (or overflows times log2 e); a descale
+                             not finite and > 0                                    */
   FA_ERR_ALIAS = 7,       /* an output or workspace overlaps an input or an output  */
   FA_ERR_OVERFLOW = 8,    /* the problem exceeds the kernel's index or grid range   */
                           /* (one head's bytes must stay below 2^31)               */

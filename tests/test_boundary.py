@@ -62,8 +62,8 @@ def test_abi_version_and_status_strings(lib):
     (dict(dtype=4), 3), (dict(dtype=-1), 3),
     (dict(d=32), 4), (dict(d=96), 4), (dict(d=256), 4), (dict(causal=2), 4), (dict(causal=-1), 4),
     (dict(q=Q + 8), 5), (dict(o=O + 2), 5), (dict(lse=L + 4), 5),
-    (dict(scale=float("nan")), 6), (dict(scale=float("inf")), 6), (dict(scale=-0.5), 6),
-    (dict(scale=3e38), 6),
+    (dict(scale=float("nan")), 6), (dict(scale=float("inf")), 6), (dict(scale=-float("inf")), 6),
+    (dict(scale=3e38), 6), (dict(scale=-3e38), 6),
     (dict(o=Q), 7), (dict(o=K + 4096), 7), (dict(lse=V + 1024), 7), (dict(lse=O + 16), 7),
     (dict(b=65536, h=65536), 8), (dict(b=2 ** 20, h=2 ** 10, n=2 ** 20), 8),
 ])
@@ -97,6 +97,15 @@ def test_lse_may_be_null_for_validation(lib):
 def test_valid_call_without_gpu_reports_hip_error(lib):
     assert call(lib) == 9
     assert lib.fa_last_hip_error() != 0
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="needs a host without a visible GPU")
+@pytest.mark.parametrize("scale", [-0.125, -1.0, -0.0, 0.0, -1e30, 1e-30])
+def test_any_finite_scale_passes_validation(lib, scale):
+    # the equation admits any finite scale (a negative one is applied as q -> -q);
+    # on a host without a GPU the call then fails only at the launch
+    assert call(lib, scale=scale) == 9
+    assert bcall(lib, scale=scale) == 9
 
 
 def block_keys(n, splits):
@@ -157,6 +166,21 @@ def test_binding_rejects_bad_tensors():
         fa.forward(x[0], x[0], x[0])  # wrong rank
 
 
+@pytest.mark.parametrize("out,lse,what", [
+    (torch.zeros(1, 1, 4, 32), None, "out"),                       # too small: would be written past its end
+    (torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16), None, "out"),  # bf16 out for f32 inputs
+    (torch.zeros(1, 1, 64, 4).transpose(2, 3), None, "out"),       # not contiguous
+    (None, torch.zeros(1, 4), "lse"),                               # lse without the batch axis
+    (None, torch.zeros(1, 1, 4, dtype=torch.float64), "lse"),
+])
+def test_binding_checks_caller_outputs_before_any_launch(out, lse, what):
+    # the C ABI sizes every write from q's shape: a caller-supplied output of
+    # another shape, type or layout is refused before anything reaches the library
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError, match=what):
+        fa.forward(x, x, x, out=out, lse=lse)
+
+
 def test_head_bytes_beyond_32_bit_buffer_range_overflow(lib):
     # one head of 2^22 rows x 128 bf16 = 1 GiB is fine; f32 doubles it past 2^31
     assert call(lib, n=(1 << 23) + 64, dtype=2) == 8
@@ -188,7 +212,7 @@ def test_backward_workspace_size(lib):
     (dict(n=0), 2), (dict(h=0), 2), (dict(wsb=100 * 2 * 4), 2),
     (dict(dtype=5), 3), (dict(dtype=0), 4), (dict(dtype=3), 4), (dict(d=96), 4), (dict(causal=2), 4),
     (dict(dq=DQ + 8), 5), (dict(lse=L + 4), 5), (dict(ws=WS + 8), 5), (dict(do=DO + 2), 5),
-    (dict(scale=float("nan")), 6), (dict(scale=-1.0), 6),
+    (dict(scale=float("nan")), 6), (dict(scale=-3e38), 6),
     (dict(dq=Q), 7), (dict(dk=OB + 64), 7), (dict(dv=DO), 7), (dict(ws=L), 7), (dict(dk=DQ), 7),
     (dict(ws=DV + 16), 7), (dict(dq=L - 64), 7),
     (dict(b=65536, h=65536), 8), (dict(n=(1 << 23) + 64), 8),

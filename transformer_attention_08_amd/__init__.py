@@ -111,6 +111,28 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _require(name: str, t: torch.Tensor, shape, dtype, device=None):
+    """A caller-supplied output or workspace tensor must be exactly what the
+    C ABI writes: the library sizes every write from q's shape, so a smaller
+    or differently typed buffer would be written past its end."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, not {t.device}")
+
+
+def _require_workspace(t: torch.Tensor, need: int, device):
+    _require("workspace", t, None, None, device)
+    if t.numel() * t.element_size() < need:
+        raise ValueError(f"workspace holds {t.numel() * t.element_size()} bytes; {need} needed")
+
+
 def _prepare(q, k, v, out, lse):
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must share one [batch, heads, n, d_k] shape")
@@ -118,10 +140,19 @@ def _prepare(q, k, v, out, lse):
         raise ValueError("q, k, v must share one dtype")
     if q.dtype not in _DTYPE_CODE:
         raise ValueError(f"unsupported dtype {q.dtype}")
+    b, h, n, d = q.shape
+    if out is not None:
+        _require("out", out, (b, h, n, d), _OUT_DTYPE[q.dtype])
+    if lse is not None:
+        _require("lse", lse, (b, h, n), torch.float32)
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous device tensors")
-    b, h, n, d = q.shape
+        if t.device != q.device:
+            raise ValueError("q, k, v must be on one device")
+    for name, t in (("out", out), ("lse", lse)):
+        if t is not None and t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device}, not {t.device}")
     if out is None:
         out = torch.empty((b, h, n, d), dtype=_OUT_DTYPE[q.dtype], device=q.device)
     if lse is None:
@@ -200,6 +231,8 @@ def forward_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, splits: O
     need = splitkv_workspace_size(b, h, n, d, splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _require_workspace(workspace, need, q.device)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     st = lib.fa_forward_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, h, n, d, s,
                                 1 if causal else 0, _DTYPE_CODE[q.dtype], int(splits),
@@ -236,11 +269,20 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     b, h, n, d = q.shape
     if lse.dtype != torch.float32 or tuple(lse.shape) != (b, h, n):
         raise ValueError("lse must be float32 [batch, heads, n]")
+    for t in (k, v, o, dout, lse):
+        if t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is not None:
+            _require(name, t, q.shape, q.dtype, q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
+    need = backward_workspace_size(b, h, n)
     if workspace is None:
-        workspace = torch.empty(backward_workspace_size(b, h, n), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    else:
+        _require_workspace(workspace, need, q.device)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     st = lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                          _ptr(dk), _ptr(dv), b, h, n, d, s, 1 if causal else 0, _DTYPE_CODE[q.dtype],
@@ -265,8 +307,11 @@ def forward_unfused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: b
         raise ValueError("forward_unfused takes float16 or bfloat16 tensors")
     out, lse = _prepare(q, k, v, out, lse)
     b, h, n, d = q.shape
+    need = unfused_workspace_size(b, h, n)
     if workspace is None:
-        workspace = torch.empty(unfused_workspace_size(b, h, n), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    else:
+        _require_workspace(workspace, need, q.device)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     st = lib.fa_forward_unfused(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, h, n, d, s,
                                 1 if causal else 0, _DTYPE_CODE[q.dtype], _ptr(workspace),
@@ -299,15 +344,27 @@ def forward_strided(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: s
         raise ValueError("q, k, v must share one 4-D shape and dtype")
     if q.dtype not in _DTYPE_CODE or not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be device tensors of a supported dtype")
+    if out_layout not in ("bhsd", "bshd"):
+        raise ValueError("out_layout is 'bhsd' or 'bshd'")
     if layout == "bhsd":
         b, h, n, d = q.shape
     else:
         b, n, h, d = q.shape
+    shape = (b, h, n, d) if out_layout == "bhsd" else (b, n, h, d)
+    for t in (k, v):
+        if t.device != q.device:
+            raise ValueError("q, k, v must be on one device")
     if out is None:
-        shape = (b, h, n, d) if out_layout == "bhsd" else (b, n, h, d)
         out = torch.empty(shape, dtype=_OUT_DTYPE[q.dtype], device=q.device)
+    else:
+        # any strides with d_k contiguous (the C ABI checks that rows do not overlap),
+        # but the extents and type the kernel writes
+        if tuple(out.shape) != shape or out.dtype != _OUT_DTYPE[q.dtype] or out.device != q.device:
+            raise ValueError(f"out must be a {_OUT_DTYPE[q.dtype]} tensor of shape {shape} on {q.device}")
     if lse is None:
         lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+    else:
+        _require("lse", lse, (b, h, n), torch.float32, q.device)
     st = [*_head_strides(q, layout), *_head_strides(k, layout), *_head_strides(v, layout),
           *_head_strides(out, out_layout)]
     arr = (ctypes.c_int64 * 12)(*st)
@@ -335,10 +392,17 @@ def forward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens
         raise ValueError("cu_seqlens must be a 1-D int32 tensor")
     total, h, d = q.shape
     batch = cu_seqlens.numel() - 1
+    for t in (k, v, cu_seqlens):
+        if t.device != q.device:
+            raise ValueError("all tensors must be on one device")
     if out is None:
         out = torch.empty((total, h, d), dtype=_OUT_DTYPE[q.dtype], device=q.device)
+    else:
+        _require("out", out, (total, h, d), _OUT_DTYPE[q.dtype], q.device)
     if lse is None:
         lse = torch.empty((h, total), dtype=torch.float32, device=q.device)
+    else:
+        _require("lse", lse, (h, total), torch.float32, q.device)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     r = lib.fa_forward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens),
                               batch, total, int(max_seqlen), h, d, s, 1 if causal else 0,
@@ -367,10 +431,15 @@ def backward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.
         raise ValueError("lse must be float32 [heads, total]")
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
         raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+    for t in (k, v, o, dout, lse, cu_seqlens):
+        if t.device != q.device:
+            raise ValueError("all tensors must be on one device")
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    need = backward_workspace_size(1, h, max(total, 1))
     if workspace is None:
-        workspace = torch.empty(max(backward_workspace_size(1, h, max(total, 1)), 16),
-                                dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _require_workspace(workspace, need, q.device)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     st = lib.fa_backward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                                 _ptr(dk), _ptr(dv), _ptr(cu_seqlens), cu_seqlens.numel() - 1, total,

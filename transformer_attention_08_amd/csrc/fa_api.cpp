@@ -28,6 +28,9 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 constexpr int64_t kMaxGrid = 0x7fffffff;
 constexpr double kLog2e = 1.4426950408889634;
 
+// Any finite scale whose product with log2(e) is a finite float.
+bool scale_ok(float scale) { return std::isfinite(scale) && std::isfinite((float)(scale * kLog2e)); }
+
 int validate(const void* q, const void* k, const void* v, void* o, const float* lse, int batch,
              int heads, int n, int d_k, float scale, int causal, int dtype) {
   if (!q || !k || !v || !o) return FA_ERR_NULL;
@@ -37,8 +40,7 @@ int validate(const void* q, const void* k, const void* v, void* o, const float* 
   const uintptr_t ptrs[5] = {(uintptr_t)q, (uintptr_t)k, (uintptr_t)v, (uintptr_t)o, (uintptr_t)lse};
   for (uintptr_t p : ptrs)
     if (p % 16) return FA_ERR_ALIGN;
-  if (!std::isfinite(scale) || scale < 0.f || !std::isfinite((float)(scale * kLog2e)))
-    return FA_ERR_SCALE;
+  if (!scale_ok(scale)) return FA_ERR_SCALE;
 
   const int64_t bh = (int64_t)batch * heads;
   const int64_t rows = bh * n;
@@ -116,8 +118,7 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
                               (uintptr_t)dv, (uintptr_t)workspace};
   for (uintptr_t p : ptrs)
     if (p % 16) return FA_ERR_ALIGN;
-  if (!std::isfinite(scale) || scale < 0.f || !std::isfinite((float)(scale * kLog2e)))
-    return FA_ERR_SCALE;
+  if (!scale_ok(scale)) return FA_ERR_SCALE;
   const int64_t bh = (int64_t)batch * heads;
   const int64_t rows = bh * n;
   if (bh > kMaxGrid || bh * (((int64_t)n + 127) / 128) > kMaxGrid) return FA_ERR_OVERFLOW;
@@ -217,12 +218,15 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int ba
     a.cu_seqlens = lay ? lay->cu_seqlens : nullptr;
     a.total = lay ? lay->total : 0;
     a.causal = causal != 0;
-    // The kernels need c > 0: a zero scale is replaced by the smallest normal
-    // float, for which every exp2 argument rounds to 0 exactly as with c = 0
-    // (uniform weights), while masked scores (-inf) still give weight 0.
-    float c = (float)(qk_scale * kLog2e);
+    // The kernels need c > 0. A negative scale is applied as q -> -q, which
+    // is exact: scale (q . k) = |scale| ((-q) . k). A zero scale is replaced
+    // by the smallest normal float, for which every exp2 argument rounds to 0
+    // exactly as with c = 0 (uniform weights), while masked scores (-inf)
+    // still give weight 0.
+    float c = (float)(std::fabs((double)qk_scale) * kLog2e);
     if (!(c > 0.f)) c = FLT_MIN;
     a.c = c;
+    a.qneg = qk_scale < 0.f;
     a.o_mult = o_mult;
     a.elt = static_cast<fa::Elt>(dtype);
     a.split_keys = n;
@@ -244,7 +248,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int ba
       cb.part_lse = a.part_lse;
       cb.o = o;
       cb.lse = lse;
-      cb.rows = batch * heads * n;
+      cb.rows = (int64_t)batch * heads * n;
       cb.d = d_k;
       cb.splits = used;
       cb.out = dtype == FA_F32 ? fa::Elt::F32 : dtype == FA_F16 ? fa::Elt::F16 : fa::Elt::BF16;
@@ -288,8 +292,11 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     a.cu_seqlens = cu_seqlens;
     a.total = total;
     a.causal = causal != 0;
+    // either sign (the kernels mask scores so that c * s = -inf); a zero
+    // scale is run as the smallest normal float, as in the forward: uniform
+    // weights while masked scores still give weight 0
     float c = (float)(scale * kLog2e);
-    if (!(c > 0.f)) c = FLT_MIN;  // as in the forward: a zero scale gives uniform weights
+    if (c == 0.f) c = FLT_MIN;
     a.c = c;
     a.scale = scale;
     a.elt = static_cast<fa::Elt>(dtype);
@@ -322,8 +329,7 @@ int fa_forward_strided(const void* q, const void* k, const void* v, void* o, flo
   if ((d_k != 64 && d_k != 128) || (causal != 0 && causal != 1)) return FA_ERR_UNSUPPORTED;
   for (uintptr_t p : {(uintptr_t)q, (uintptr_t)k, (uintptr_t)v, (uintptr_t)o, (uintptr_t)lse})
     if (p % 16) return FA_ERR_ALIGN;
-  if (!std::isfinite(scale) || scale < 0.f || !std::isfinite((float)(scale * kLog2e)))
-    return FA_ERR_SCALE;
+  if (!scale_ok(scale)) return FA_ERR_SCALE;
   const int ib = elt_bytes_in(dtype), ob = elt_bytes_out(dtype);
   for (int i = 0; i < 12; ++i) {
     const int eb = i < 9 ? ib : ob;
@@ -369,8 +375,7 @@ int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, floa
   for (uintptr_t p : {(uintptr_t)q, (uintptr_t)k, (uintptr_t)v, (uintptr_t)o, (uintptr_t)lse})
     if (p % 16) return FA_ERR_ALIGN;
   if ((uintptr_t)cu_seqlens % 4) return FA_ERR_ALIGN;
-  if (!std::isfinite(scale) || scale < 0.f || !std::isfinite((float)(scale * kLog2e)))
-    return FA_ERR_SCALE;
+  if (!scale_ok(scale)) return FA_ERR_SCALE;
   const int ib = elt_bytes_in(dtype), ob = elt_bytes_out(dtype);
   const int64_t rs = (int64_t)heads * d_k;  // row stride, elements
   if (((int64_t)max_seqlen + 256) * rs * std::max(ib, ob) > INT32_MAX) return FA_ERR_OVERFLOW;
@@ -450,6 +455,7 @@ int fa_forward_splitkv(const void* q, const void* k, const void* v, void* o, flo
     const size_t need = split_layout(batch, heads, n, d_k, used).total;
     if (workspace_bytes < need) return FA_ERR_SHAPE;
     const int64_t rows = (int64_t)batch * heads * n;
+    if (rows > INT32_MAX) return FA_ERR_OVERFLOW;  // the merge kernel's grid
     const int in_bytes = dtype == FA_F32 ? 4 : dtype == FA_FP8_E4M3 ? 1 : 2;
     const int out_bytes = dtype == FA_F32 ? 4 : 2;
     const Range rw{(uintptr_t)workspace, (uintptr_t)workspace + need};
@@ -550,8 +556,7 @@ int fa_backward_varlen(const void* q, const void* k, const void* v, const void* 
                       (uintptr_t)workspace})
     if (p % 16) return FA_ERR_ALIGN;
   if ((uintptr_t)cu_seqlens % 4) return FA_ERR_ALIGN;
-  if (!std::isfinite(scale) || scale < 0.f || !std::isfinite((float)(scale * kLog2e)))
-    return FA_ERR_SCALE;
+  if (!scale_ok(scale)) return FA_ERR_SCALE;
   const int64_t rs = (int64_t)heads * d_k;  // row stride, elements
   if (((int64_t)max_seqlen + 256) * rs * 2 > INT32_MAX) return FA_ERR_OVERFLOW;
   const int64_t bh = (int64_t)batch * heads;
@@ -588,7 +593,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_DTYPE: return "unknown dtype";
     case FA_ERR_UNSUPPORTED: return "unsupported d_k (64 or 128), causal flag (0 or 1), split count or backward dtype";
     case FA_ERR_ALIGN: return "pointer not 16-byte aligned";
-    case FA_ERR_SCALE: return "scale or descale not finite, or negative";
+    case FA_ERR_SCALE: return "scale not finite (or scale * log2(e) overflows), or a descale not finite and positive";
     case FA_ERR_ALIAS: return "an output or workspace overlaps an input or another output";
     case FA_ERR_OVERFLOW: return "problem exceeds the kernel's index or grid range";
     case FA_ERR_HIP: return "HIP runtime error (see fa_last_hip_error)";

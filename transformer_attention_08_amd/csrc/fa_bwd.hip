@@ -192,8 +192,8 @@ void bwd_dq(BwdArgs a) {
   // only when every first tile's key-tile count is a multiple of NS, so the
   // second tile starts on slot 0.
   const bool pair = a.pair;
-  const TileId tl = pair ? tile_of_block(blockIdx.x, a.bh, tiles / 2, false, tiles)
-                         : tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
+  const TileId tl = pair ? tile_of_block(blockIdx.x, a.bh, tiles / 2, false, kDqBq, tiles)
+                         : tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL, kDqBq);
   const BwdView hv = bwd_view(a, tl.bh);
   const int n = hv.n;
   int q0 = (pair ? tiles - 1 - tl.t : tl.t) * kDqBq;
@@ -259,6 +259,8 @@ void bwd_dq(BwdArgs a) {
   const int tcol = 16 * (grp & 1) + 4 * (li & 3);  // + db*32
 
   const float c = a.c;
+  // a masked score must give c * s = -inf whatever the sign of c
+  const float s_masked = c > 0.f ? -INFINITY : INFINITY;
   f32x16_t dq[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dq[db] = f32x16_t{};
@@ -284,7 +286,7 @@ void bwd_dq(BwdArgs a) {
         for (int i = 0; i < 16; ++i) {
           const int key = j * BK + kb * 32 + 16 * (i >> 3) + 8 * hl + (i & 7);
           const bool ok = key < n && (!CAUSAL || key <= qrow);
-          s[i] = ok ? s[i] : -INFINITY;
+          s[i] = ok ? s[i] : s_masked;
         }
       }
       u32x4_t dsb[2];
@@ -401,7 +403,7 @@ void bwd_dkdv(BwdArgs a) {
   const int lane = tid & 63, lr = lane & 31, hl = lane >> 5;
   const int ktiles = (a.n + kKvBk - 1) / kKvBk;
   // ascending key tiles: under a causal mask the first ones see the most queries
-  const TileId tl = tile_of_block(blockIdx.x, a.bh, ktiles, false);
+  const TileId tl = tile_of_block(blockIdx.x, a.bh, ktiles, false, kKvBk);
   const BwdView hv = bwd_view(a, tl.bh);
   const int n = hv.n;
   const int k0 = tl.t * kKvBk;
@@ -459,6 +461,7 @@ void bwd_dkdv(BwdArgs a) {
   const int tcol = 16 * (grp & 1) + 4 * (li & 3);
 
   const float c = a.c;
+  const float s_masked = c > 0.f ? -INFINITY : INFINITY;  // c * s_masked = -inf
   f32x16_t dk[NDB], dv[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = f32x16_t{};
@@ -516,7 +519,7 @@ void bwd_dkdv(BwdArgs a) {
         for (int r = 0; r < 16; ++r) {
           const int q_ = it * kKvBq + qb * 32 + 16 * (r >> 3) + 8 * hl + (r & 7);
           const bool ok = key < n && (!CAUSAL || key <= q_);
-          sc[r] = ok ? sc[r] : -INFINITY;
+          sc[r] = ok ? sc[r] : s_masked;
         }
       }
       u32x4_t pb[2], dsb[2];
@@ -594,17 +597,6 @@ void bwd_dkdv(BwdArgs a) {
 #endif
 
 // Compute units of the current device, read once per device.
-int bwd_device_cus() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int cus = cached[dev].load(std::memory_order_relaxed);
-  if (cus == 0) {
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    cached[dev].store(cus, std::memory_order_relaxed);
-  }
-  return cus;
-}
 
 template <Elt E, int D>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
@@ -614,21 +606,18 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   // a mask, while the paired grid still covers every CU.
   BwdArgs b = a;
   b.pair = !a.cu_seqlens && tiles % 2 == 0 && a.n % kDqBq == 0 && (kDqBq / FA_BWD_TILE) % kBwdStages == 0 &&
-           FA_BWD_PAIR && (a.causal || (long)a.bh * (tiles / 2) >= bwd_device_cus());
+           FA_BWD_PAIR && (a.causal || (long)a.bh * (tiles / 2) >= device_cus());
   const unsigned g1 = (unsigned)a.bh * (unsigned)(b.pair ? tiles / 2 : tiles);
   const unsigned g2 = (unsigned)a.bh * (unsigned)((a.n + kKvBk - 1) / kKvBk);
   if (a.causal) {
-    hipLaunchKernelGGL((bwd_dq<E, D, true>), dim3(g1), dim3(kDqThreads), 0, s, b);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_kernel(bwd_dq<E, D, true>, dim3(g1), dim3(kDqThreads), s, b);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv<E, D, true>), dim3(g2), dim3(kKvThreads), 0, s, a);
+    return launch_kernel(bwd_dkdv<E, D, true>, dim3(g2), dim3(kKvThreads), s, a);
   } else {
-    hipLaunchKernelGGL((bwd_dq<E, D, false>), dim3(g1), dim3(kDqThreads), 0, s, b);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_kernel(bwd_dq<E, D, false>, dim3(g1), dim3(kDqThreads), s, b);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv<E, D, false>), dim3(g2), dim3(kKvThreads), 0, s, a);
+    return launch_kernel(bwd_dkdv<E, D, false>, dim3(g2), dim3(kKvThreads), s, a);
   }
-  return hipGetLastError();
 }
 
 }  // namespace

@@ -37,19 +37,21 @@ struct TileId {
 // one sequence of a ragged batch -- spread over all XCDs. Each XCD takes its
 // heads in groups of G, the longest tiles of a group first: a head's
 // workgroups then run close together and re-read its K/V tiles from L2
-// rather than HBM. Heads of 64 tiles or more go one at a time (a head's
-// keys then stream through the XCD in fewer rounds of its CUs), heads of 32
-// to 63 tiles in groups of 2; short ones in one group, where the longest
-// tiles of every head going first matters more for the tail than the
-// re-reads. head_tiles (when not negative) is the
-// head's length in tiles for that choice, when a workgroup holds more than
-// one tile.
-__device__ inline TileId tile_of_block(int pid, int bh_count, int tiles, bool reverse, int head_tiles = -1) {
+// rather than HBM. The group size depends on the head's length in rows (the
+// same rule for every kernel, whatever its tile size): heads of 16384 rows
+// or more go one at a time (a head's keys then stream through the XCD in
+// fewer rounds of its CUs), heads of 8192 to 16383 rows in groups of 2,
+// shorter ones in one group, where the longest tiles of every head going
+// first matters more for the tail than the re-reads. tile_rows is the
+// calling kernel's rows (or keys) per tile; head_tiles (when not negative)
+// is the head's length in such tiles when a workgroup holds more than one.
+__device__ inline TileId tile_of_block(int pid, int bh_count, int tiles, bool reverse, int tile_rows,
+                                       int head_tiles = -1) {
   int bh, tt;
   if ((bh_count & 7) == 0) {
     const int xcd = pid & 7, slot = pid >> 3, per = bh_count >> 3;
-    const int ht = head_tiles < 0 ? tiles : head_tiles;
-    const int G = ht >= 64 ? 1 : (ht >= 32 && (per & 1) == 0) ? 2 : per;
+    const int rows = (head_tiles < 0 ? tiles : head_tiles) * tile_rows;
+    const int G = rows >= 16384 ? 1 : (rows >= 8192 && (per & 1) == 0) ? 2 : per;
     const int g = slot / (G * tiles), r = slot - g * (G * tiles);
     tt = r / G;
     bh = (g * G + r % G) * 8 + xcd;
@@ -146,6 +148,16 @@ template <int N>
 __device__ inline void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Enqueue kernel(a) and return the status of this launch itself (never a
+// stale error that an earlier, unrelated HIP call left on the thread, which
+// hipGetLastError would report -- and clear -- instead).
+template <typename A>
+inline hipError_t launch_kernel(void (*kernel)(A), dim3 grid, dim3 block, hipStream_t stream, const A& a) {
+  A arg = a;
+  void* args[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, stream);
 }
 
 }  // namespace

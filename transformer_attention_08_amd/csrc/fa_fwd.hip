@@ -276,8 +276,8 @@ void fwd_direct(FwdArgs a) {
   // its K/V ring runs on from the first tile's keys into the second's, so
   // the second tile starts with its first keys already in LDS.
   const bool pair = a.pair;
-  const TileId tl = pair ? tile_of_block(blockIdx.x, a.bh, tiles / 2, false, tiles)
-                         : tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
+  const TileId tl = pair ? tile_of_block(blockIdx.x, a.bh, tiles / 2, false, kDirectBq, tiles)
+                         : tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL, kDirectBq);
   const HeadView hv = head_view<2, 2>(a, tl.bh);
   const int n = hv.n;
   int q0 = (pair ? tiles - 1 - tl.t : tl.t) * kDirectBq;
@@ -327,6 +327,12 @@ void fwd_direct(FwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
       qf[ks] = bload16(rq, (uint32_t)qrow * hv.qrs + (ks * 16 + hl * 8) * 2);
+    // a negative scale: q -> -q (the sign bits; uniform branch, so the loads
+    // are waited for here only in that case)
+    if (a.qneg) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qf[ks] ^= 0x80008000u;
+    }
   };
   load_q();
 
@@ -549,7 +555,7 @@ void fwd_direct8(FwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 31, hl = lane >> 5;
   const int tiles = (a.n + kDirectBq - 1) / kDirectBq;
-  const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
+  const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL, kDirectBq);
   const HeadView hv = head_view<1, 2>(a, tl.bh);
   const int n = hv.n;
   const int q0 = tl.t * kDirectBq;
@@ -712,9 +718,11 @@ void fwd_direct8(FwdArgs a) {
   issue(j_lo);
   wait_vmcnt<0>();
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks)
+  for (int ks = 0; ks < NKS; ++ks) {
     qf[ks] = u32x4_t{e4m3x2_to_bf16x2<false>(q8[ks][0]), e4m3x2_to_bf16x2<true>(q8[ks][0]),
                      e4m3x2_to_bf16x2<false>(q8[ks][1]), e4m3x2_to_bf16x2<true>(q8[ks][1])};
+    if (a.qneg) qf[ks] ^= 0x80008000u;  // a negative scale: q -> -q
+  }
   __syncthreads();
   widen(ring0);
   __syncthreads();
@@ -770,7 +778,7 @@ void fwd_mfma32(FwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, provably uniform
   const int lane = tid & 63, lr = lane & 31, hl = lane >> 5;
   const int tiles = (a.n + kBq - 1) / kBq;
-  const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL);
+  const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL, kBq);
   const HeadView hv = head_view<4, 4>(a, tl.bh);
   const int n = hv.n;
   const int q0 = tl.t * kBq;
@@ -790,7 +798,8 @@ void fwd_mfma32(FwdArgs a) {
     for (int i = 0; i < HALF / 4; ++i) {
       u32x4_t x = qp[i];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qf[4 * i + e] = ok ? __uint_as_float(x[e]) : 0.f;
+      for (int e = 0; e < 4; ++e)  // a negative scale: q -> -q
+        qf[4 * i + e] = ok ? __uint_as_float(x[e] ^ (a.qneg ? 0x80000000u : 0u)) : 0.f;
     }
   }
 
@@ -912,13 +921,11 @@ void fwd_mfma32(FwdArgs a) {
   }
 }
 
-template <typename K>
-hipError_t launch(K kernel, const FwdArgs& a, hipStream_t stream, int rows = kBq,
+hipError_t launch(void (*kernel)(FwdArgs), const FwdArgs& a, hipStream_t stream, int rows = kBq,
                   int threads = kThreads) {
   const int tiles = (a.n + rows - 1) / rows;
   const unsigned grid = (unsigned)a.bh * (unsigned)tiles;
-  hipLaunchKernelGGL(kernel, dim3(grid, (unsigned)a.splits), dim3(threads), 0, stream, a);
-  return hipGetLastError();
+  return launch_kernel(kernel, dim3(grid, (unsigned)a.splits), dim3(threads), stream, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -934,10 +941,10 @@ constexpr int kCombineRows = 256 / (D / 4);
 template <Elt OUT, int D>
 __global__ __launch_bounds__(256) void combine_splits(CombineArgs a) {
   constexpr int kLanesPerRow = D / 4;
-  const int row = blockIdx.x * kCombineRows<D> + (int)threadIdx.x / kLanesPerRow;
+  const int64_t row = (int64_t)blockIdx.x * kCombineRows<D> + (int)threadIdx.x / kLanesPerRow;
   const int col = ((int)threadIdx.x % kLanesPerRow) * 4;
   if (row >= a.rows) return;
-  const size_t plane = (size_t)a.rows;  // rows per split
+  const int64_t plane = a.rows;  // rows per split
   float mx = -INFINITY;
   for (int g = 0; g < a.splits; ++g) mx = fmaxf(mx, a.part_lse[g * plane + row]);
   // every row has a visible key in some block, so mx is finite
@@ -975,26 +982,12 @@ template <Elt OUT>
 hipError_t launch_combine_t(const CombineArgs& a, hipStream_t s) {
   if (a.d == 64) {
     const unsigned grid = (unsigned)((a.rows + kCombineRows<64> - 1) / kCombineRows<64>);
-    hipLaunchKernelGGL((combine_splits<OUT, 64>), dim3(grid), dim3(256), 0, s, a);
-  } else {
-    const unsigned grid = (unsigned)((a.rows + kCombineRows<128> - 1) / kCombineRows<128>);
-    hipLaunchKernelGGL((combine_splits<OUT, 128>), dim3(grid), dim3(256), 0, s, a);
+    return launch_kernel(combine_splits<OUT, 64>, dim3(grid), dim3(256), s, a);
   }
-  return hipGetLastError();
+  const unsigned grid = (unsigned)((a.rows + kCombineRows<128> - 1) / kCombineRows<128>);
+  return launch_kernel(combine_splits<OUT, 128>, dim3(grid), dim3(256), s, a);
 }
 
-// Compute units of the current device (256 on MI355X), read once per device.
-int device_cus() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int cus = cached[dev].load(std::memory_order_relaxed);
-  if (cus == 0) {
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    cached[dev].store(cus, std::memory_order_relaxed);
-  }
-  return cus;
-}
 
 template <Elt E, int D>
 hipError_t dispatch_causal(const FwdArgs& a, hipStream_t s) {
@@ -1013,11 +1006,8 @@ hipError_t dispatch_causal(const FwdArgs& a, hipStream_t s) {
       FwdArgs b = a;
       b.pair = 1;
       const dim3 grid((unsigned)a.bh * (unsigned)(tiles / 2), 1u);
-      if (a.causal)
-        hipLaunchKernelGGL((fwd_direct<E, D, true>), grid, dim3(kDirectThreads), 0, s, b);
-      else
-        hipLaunchKernelGGL((fwd_direct<E, D, false>), grid, dim3(kDirectThreads), 0, s, b);
-      return hipGetLastError();
+      return a.causal ? launch_kernel(fwd_direct<E, D, true>, grid, dim3(kDirectThreads), s, b)
+                      : launch_kernel(fwd_direct<E, D, false>, grid, dim3(kDirectThreads), s, b);
     }
     return a.causal ? launch(fwd_direct<E, D, true>, a, s, kDirectBq, kDirectThreads)
                     : launch(fwd_direct<E, D, false>, a, s, kDirectBq, kDirectThreads);
@@ -1030,6 +1020,19 @@ hipError_t dispatch_d(const FwdArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Compute units of the current device (256 on MI355X), read once per device.
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
+}
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   switch (a.out) {

@@ -31,7 +31,12 @@ struct FwdArgs {
   const int* cu_seqlens;
   int total;
   bool causal;
-  float c;         // scale (times both fp8 descales) times log2(e)
+  // c = |scale| (times both fp8 descales) times log2(e), > 0. A negative
+  // scale is applied as q -> -q (exact in every element type): then
+  // scale (q . k) = |scale| ((-q) . k), and the kernels' row max of c s is
+  // the max of the scaled scores.
+  float c;
+  bool qneg = false;
   float o_mult;    // multiplier applied to O in the epilogue (v descale; 1 otherwise)
   Elt elt;
   // Split-KV: the keys are cut into blocks of split_keys (a multiple of 128;
@@ -55,7 +60,7 @@ struct CombineArgs {
   const float* part_lse;
   void* o;
   float* lse;      // may be null
-  int rows;        // batch * heads * n
+  int64_t rows;    // batch * heads * n
   int d;
   int splits;
   Elt out;         // F32, F16 or BF16
@@ -88,7 +93,7 @@ struct BwdArgs {
   const int* cu_seqlens;
   int total;
   bool causal;
-  float c;            // scale * log2(e)
+  float c;            // scale * log2(e); either sign (never 0: a zero scale is run as FLT_MIN)
   float scale;
   Elt elt;            // F16 or BF16
   // Paired query tiles in the dQ pass (as FwdArgs::pair; set by the launcher).
@@ -123,5 +128,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
 // Enqueue the three unfused kernels (scores, row softmax, P V).
 hipError_t launch_unfused(const UnfArgs& a, hipStream_t stream);
+// Compute units of the current device (256 on MI355X), read once per device.
+int device_cus();
 
 }  // namespace fa

@@ -194,17 +194,12 @@ template <Elt E, int D>
 hipError_t launch_unf_t(const UnfArgs& a, hipStream_t s) {
   const unsigned g13 = (unsigned)a.bh * (unsigned)((a.n + 127) / 128);
   const unsigned g2 = (unsigned)((a.rows + kUnfWaves - 1) / kUnfWaves);
-  if (a.causal)
-    hipLaunchKernelGGL((unf_scores<E, D, true>), dim3(g13), dim3(kUnfThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((unf_scores<E, D, false>), dim3(g13), dim3(kUnfThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
+  hipError_t e = a.causal ? launch_kernel(unf_scores<E, D, true>, dim3(g13), dim3(kUnfThreads), s, a)
+                          : launch_kernel(unf_scores<E, D, false>, dim3(g13), dim3(kUnfThreads), s, a);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((unf_softmax<E>), dim3(g2), dim3(kUnfThreads), 0, s, a);
-  e = hipGetLastError();
+  e = launch_kernel(unf_softmax<E>, dim3(g2), dim3(kUnfThreads), s, a);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((unf_pv<E, D>), dim3(g13), dim3(kUnfThreads), 0, s, a);
-  return hipGetLastError();
+  return launch_kernel(unf_pv<E, D>, dim3(g13), dim3(kUnfThreads), s, a);
 }
 
 }  // namespace
