@@ -9,7 +9,8 @@ arithmetic is not counted: the same slide treats scale/mask/softmax as a
 bytes-bound step, not a FLOP-bound one.
 
 Bytes: the unavoidable HBM traffic of a fused kernel -- read Q, K, V once,
-write O and the per-row log-sum-exp (fp32) once.
+write O and the per-row log-sum-exp (fp32) once. O is written in the input
+type, except for e4m3 inputs, whose O is bf16.
 """
 from __future__ import annotations
 
@@ -21,9 +22,13 @@ def flops(batch: int, heads: int, n: int, d_k: int, causal: bool) -> float:
     return f / 2.0 if causal else f
 
 
-def exp_count(batch: int, heads: int, n: int, causal: bool) -> float:
-    e = float(batch) * heads * n * n
-    return e / 2.0 if causal else e
+def exp_count(batch: int, heads: int, n: int, causal: bool) -> int:
+    """Exponentials the method evaluates: one per visible (query, key) pair,
+    i.e. per entry of P that the mask leaves in place -- n * n per head, or
+    n (n + 1) / 2 under the causal mask (query i sees keys 0 .. i). Exact,
+    not the halved FLOP convention."""
+    per_head = n * (n + 1) // 2 if causal else n * n
+    return int(batch) * int(heads) * per_head
 
 
 def min_hbm_bytes(batch: int, heads: int, n: int, d_k: int, in_dtype: str, out_dtype: str,

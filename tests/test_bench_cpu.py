@@ -5,12 +5,14 @@ import os
 import subprocess
 import sys
 
+import pytest
 import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
+import oracle  # noqa: E402
 import workload  # noqa: E402
 
 
@@ -20,6 +22,29 @@ def test_llama_accounting():
     assert bench.algorithmic_flops(w) == 4 * 32 * 8192 ** 2 * 128 / 2 == 5.49755813888e11
     assert bench.min_hbm_bytes(w) == 269484032
     assert bench.backward_flops(w) == 2.5 * bench.algorithmic_flops(w)
+
+
+@pytest.mark.parametrize("name", sorted(workload.WORKLOADS))
+def test_roofline_denominators_match_an_independent_count(name):
+    """bench.py keeps its own FLOP and byte counts (it may not import the
+    oracle outside its CPU-baseline leg). Both are pinned here for every
+    workload: the bytes against the sizes of the tensors the generator makes
+    plus the O and LSE tensors bench.py allocates for them, the FLOPs against
+    the two products of one head counted on a tiny case and scaled, and both
+    against the oracle's own accounting."""
+    w = workload.WORKLOADS[name]
+    rows = 16
+    inp = workload.make_inputs(1, 1, rows, w.d_k, w.dtype, seed=0)
+    o = torch.empty(1, 1, rows, w.d_k, dtype=workload.torch_dtype(w.out_dtype))
+    lse = torch.empty(1, 1, rows, dtype=torch.float32)
+    per_row = sum(t.numel() * t.element_size() for t in (inp.q, inp.k, inp.v, o, lse)) // rows
+    assert bench.min_hbm_bytes(w) == w.batch * w.heads * w.n * per_row
+    assert bench.min_hbm_bytes(w) == oracle.min_hbm_bytes(w.batch, w.heads, w.n, w.d_k, w.dtype, w.out_dtype)
+    # S = Q K^T and O = P V: 2 n d_k FLOP per (query, key) each, over all n^2
+    # pairs, halved by convention under the causal mask
+    pairs = w.n * w.n
+    assert bench.algorithmic_flops(w) == w.batch * w.heads * 2 * (2 * w.d_k) * pairs / (2 if w.causal else 1)
+    assert bench.algorithmic_flops(w) == oracle.flops(w.batch, w.heads, w.n, w.d_k, w.causal)
 
 
 def test_more_than_one_gpu_is_refused():

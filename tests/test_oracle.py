@@ -316,8 +316,46 @@ def test_accounting_matches_the_slides():
     assert f == 4 * 32 * 8192 ** 2 * 128
     assert oracle.score_matrix_ratio(g["n"], g["d_k"]) == g["s_p_over_qkvo"]
     assert oracle.flops(1, 32, 8192, 128, causal=True) == f / 2
-    # Q+K+V+O in bf16 plus fp32 LSE
-    assert oracle.min_hbm_bytes(1, 32, 8192, 128, "bf16", "bf16") == 4 * 32 * 8192 * 128 * 2 + 4 * 32 * 8192
+
+
+# element type of O for each input type (include/fa.h: e4m3 inputs give bf16 O)
+OUT_OF = {"f32": "f32", "f16": "f16", "bf16": "bf16", "fp8": "bf16"}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "fp8"])
+@pytest.mark.parametrize("shape", [(1, 1, 256, 64), (2, 3, 100, 128), (1, 32, 8192, 128), (2, 32, 2048, 128)])
+def test_min_hbm_bytes_is_the_size_of_the_tensors(shape, dtype):
+    """min_hbm_bytes against an independent count: the bytes of the Q, K, V
+    tensors the input generator makes, plus those of the O and fp32 LSE
+    tensors a caller allocates for them (e4m3 in, bf16 out included)."""
+    b, h, n, d = shape
+    small = (b, h, min(n, 64), d)
+    inp = workload.make_inputs(*small, dtype, seed=0)
+    per_row_in = sum(t.numel() * t.element_size() for t in (inp.q, inp.k, inp.v)) // (b * h * small[2])
+    o = torch.empty(small, dtype=workload.torch_dtype(OUT_OF[dtype]))
+    lse = torch.empty(small[:3], dtype=torch.float32)
+    per_row_out = (o.numel() * o.element_size() + lse.numel() * lse.element_size()) // (b * h * small[2])
+    assert oracle.min_hbm_bytes(b, h, n, d, dtype, OUT_OF[dtype]) == b * h * n * (per_row_in + per_row_out)
+    # without the LSE, Q + K + V + O alone
+    assert oracle.min_hbm_bytes(b, h, n, d, dtype, OUT_OF[dtype], with_lse=False) == \
+        b * h * n * (per_row_in + o.element_size() * d)
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 33])
+@pytest.mark.parametrize("causal", [False, True])
+def test_exp_count_is_the_number_of_visible_entries_of_p(n, causal):
+    """exp_count against the materialised P of the oracle: one exponential per
+    entry the mask leaves visible (the others are exp(-inf) = 0, never
+    evaluated)."""
+    b, h, d = 2, 3, 16
+    q, k, v = (rnd((b, h, n, d), 300 + i) for i in range(3))
+    _, _, p = oracle.attention(q, k, v, 0.25, causal, return_p=True)
+    s = 0.25 * np.einsum("bhid,bhjd->bhij", q, k)
+    if causal:
+        s = np.where(np.triu(np.ones((n, n), bool), 1), -np.inf, s)
+    visible = int(np.isfinite(s).sum())
+    assert (p[np.isfinite(s)] > 0).all() and (p[~np.isfinite(s)] == 0).all()
+    assert oracle.exp_count(b, h, n, causal) == visible
 
 
 # ---------------------------------------------------------------- planted mistakes
