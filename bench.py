@@ -20,6 +20,8 @@ that no input is served from the L2s or the 256 MB Infinity Cache
     python bench.py --layout bshd   # [batch, n, heads, d_k] inputs (fa_forward_strided)
     python bench.py --varlen 16     # a ragged batch of 16 sequences (fa_forward_varlen)
     python bench.py --copy-calibration      # plain copy of known size (counter scale)
+    python bench.py --mfma-rate             # issue rate of the 32x32x16 and 16x16x32 MFMAs
+    python bench.py --lds-rate              # LDS read bandwidth (16-byte and transposing reads)
 """
 from __future__ import annotations
 
@@ -82,6 +84,18 @@ def stored_traffic(workload_name: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def host_threads():
+    """(cores this process may run on, threads of the BLAS that NumPy calls)."""
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+                   or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    return cores, int(blas)
+
+
 def cpu_baseline(w, inp, budget_s: float = 15.0):
     """The fp64 oracle on whole heads of the same inputs, as many heads as fit
     the time budget (at least one); TFLOP/s under the same FLOP count."""
@@ -89,11 +103,7 @@ def cpu_baseline(w, inp, budget_s: float = 15.0):
 
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    cores, blas = host_threads()
     qb, kb, vb = inp.bits("q"), inp.bits("k"), inp.bits("v")
     done, elapsed = 0, 0.0
     while done < w.heads * w.batch:
@@ -108,9 +118,11 @@ def cpu_baseline(w, inp, budget_s: float = 15.0):
         if elapsed >= budget_s or elapsed / done * (done + 1) > 2 * budget_s:
             break
     fl = 4.0 * done * w.n * w.n * w.d_k / (2 if w.causal else 1)
-    return {"value": fl / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": fl / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "blas_threads": blas,
+            "kind": "oracle",
             "sample": f"{done} of {w.batch * w.heads} heads, all {w.n} rows each, fp64 NumPy, "
-                      f"{elapsed:.1f} s"}
+                      f"{elapsed:.1f} s; the products run on {blas} BLAS threads, the exponentials "
+                      f"(NumPy exp) on one thread, heads one after another"}
 
 
 def cpu_baseline_backward(w, inp, do, budget_s: float = 15.0):
@@ -119,11 +131,7 @@ def cpu_baseline_backward(w, inp, do, budget_s: float = 15.0):
     TFLOP/s under the backward FLOP count."""
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    cores, blas = host_threads()
     qb, kb, vb = inp.bits("q"), inp.bits("k"), inp.bits("v")
     gb = do.contiguous().view(__import__("torch").int16).numpy().view("uint16")
     done, elapsed = 0, 0.0
@@ -137,9 +145,11 @@ def cpu_baseline_backward(w, inp, do, budget_s: float = 15.0):
         if elapsed >= budget_s or elapsed / done * (done + 1) > 2 * budget_s:
             break
     fl = 10.0 * done * w.n * w.n * w.d_k / (2 if w.causal else 1)
-    return {"value": fl / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": fl / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "blas_threads": blas,
+            "kind": "oracle",
             "sample": f"{done} of {w.batch * w.heads} heads, all {w.n} rows each, fp64 NumPy "
-                      f"(S, P, dP, dS materialised), {elapsed:.1f} s"}
+                      f"(S, P, dP, dS materialised), {elapsed:.1f} s; the products run on {blas} BLAS "
+                      f"threads, the exponentials on one thread"}
 
 
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
@@ -152,6 +162,87 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
         y.copy_(x)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}))
+
+
+MFMA_KINDS = ((0, "v_mfma_f32_32x32x16_bf16", 32 * 32 * 16 * 2),
+              (1, "v_mfma_f32_16x16x32_bf16", 16 * 16 * 32 * 2),
+              (2, "v_mfma_f32_32x32x16_f16", 32 * 32 * 16 * 2),
+              (3, "v_mfma_f32_16x16x32_f16", 16 * 16 * 32 * 2))
+
+
+def mfma_rate(iters: int = 2000, blocks: int = 256):
+    """Issue rate of the 16-bit MFMAs with independent accumulators (the
+    libfa_probe.so kernel: one workgroup per CU, 1 or 2 waves per SIMD, no
+    memory traffic in the timed loop). One JSON line per variant: shader
+    cycles per MFMA on a SIMD, FLOP per cycle per SIMD (1024 at the dense
+    peak), and the shader clock from the wave's own cycle and 100 MHz
+    counters."""
+    import ctypes
+
+    import torch
+
+    from transformer_attention_08_amd import build as _b
+
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    lib.fa_probe_mfma_rate.restype = ctypes.c_int
+    lib.fa_probe_mfma_rate.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p] * 3
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(512, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for kind, name, flop in MFMA_KINDS:
+        for wps in (1, 2):
+            for nacc in (1, 2, 4, 8):
+                out = torch.zeros(2 * blocks * 4 * wps, dtype=torch.int64, device=dev)
+                for _ in range(2):  # the first launch warms the clock
+                    rc = lib.fa_probe_mfma_rate(kind, nacc, wps, blocks, iters, out.data_ptr(),
+                                                sink.data_ptr(), stream.cuda_stream)
+                    if rc != 0:
+                        raise RuntimeError(f"probe launch failed: hipError {rc}")
+                    torch.cuda.synchronize(dev)
+                cyc = out[0::2].double().cpu().view(blocks, 4 * wps)
+                ticks = out[1::2].double().cpu().view(blocks, 4 * wps)
+                per_wave = 4 * nacc * iters
+                # a SIMD runs wps waves side by side: the workgroup's longest
+                # wave over the MFMAs one SIMD issues
+                c_simd = float(cyc.max(dim=1).values.median()) / (wps * per_wave)
+                ghz = float((cyc / (ticks / 100e6)).median()) / 1e9
+                print(json.dumps({"probe": "mfma_rate", "instruction": name, "waves_per_simd": wps,
+                                  "accumulators": nacc, "cycles_per_mfma_per_simd": round(c_simd, 2),
+                                  "flop_per_clk_per_simd": round(flop / c_simd, 1),
+                                  "shader_ghz": round(ghz, 3)}), flush=True)
+
+
+def lds_rate(iters: int = 4000, blocks: int = 256):
+    """LDS read bandwidth per CU (the libfa_probe.so kernel: one workgroup per
+    CU, 4 or 8 waves each issuing rounds of 8 independent reads) for
+    ds_read_b128 and the transposing ds_read_b64_tr_b16. One JSON line per
+    variant: bytes per shader cycle per CU, and the shader clock."""
+    import ctypes
+
+    import torch
+
+    from transformer_attention_08_amd import build as _b
+
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    lib.fa_probe_lds_rate.restype = ctypes.c_int
+    lib.fa_probe_lds_rate.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    for mode, name, per_read in ((0, "ds_read_b128", 16 * 64), (1, "ds_read_b64_tr_b16", 8 * 64)):
+        for waves in (4, 8):
+            out = torch.zeros(2 * blocks * waves, dtype=torch.int64, device=dev)
+            for _ in range(2):
+                rc = lib.fa_probe_lds_rate(mode, waves, blocks, iters, out.data_ptr(), stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"probe launch failed: hipError {rc}")
+                torch.cuda.synchronize(dev)
+            cyc = out[0::2].double().cpu().view(blocks, waves)
+            ticks = out[1::2].double().cpu().view(blocks, waves)
+            c_block = float(cyc.max(dim=1).values.median())
+            ghz = float((cyc / (ticks / 100e6)).median()) / 1e9
+            print(json.dumps({"probe": "lds_rate", "instruction": name, "waves_per_cu": waves,
+                              "bytes_per_clk_per_cu": round(waves * 8 * iters * per_read / c_block, 1),
+                              "shader_ghz": round(ghz, 3)}), flush=True)
 
 
 def backward_flops(w) -> float:
@@ -349,6 +440,10 @@ def main(argv=None):
     ap.add_argument("--no-cold-cache", action="store_true",
                     help="skip the second pass that reads 512 MiB of other device memory before each call")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--mfma-rate", action="store_true",
+                    help="issue rate of the 32x32x16 and 16x16x32 MFMAs (libfa_probe.so)")
+    ap.add_argument("--lds-rate", action="store_true",
+                    help="LDS read bandwidth of ds_read_b128 and ds_read_b64_tr_b16 (libfa_probe.so)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -359,6 +454,12 @@ def main(argv=None):
 
     if args.copy_calibration:
         copy_calibration()
+        return 0
+    if args.mfma_rate:
+        mfma_rate()
+        return 0
+    if args.lds_rate:
+        lds_rate()
         return 0
 
     import torch

@@ -15,6 +15,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
 SOURCES = ("fa_fwd.hip", "fa_bwd.hip", "fa_unfused.hip", "fa_api.cpp")
+# the matrix-core rate probe behind `bench.py --mfma-rate`; a library of its own
+PROBE_LIB = os.path.join(PKG, "libfa_probe.so")
+PROBE_SOURCES = ("fa_probe.hip",)
 ARCH = "gfx950"
 
 
@@ -25,8 +28,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def compile_command(out: str = LIB, extra=()) -> list:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+def compile_command(out: str = LIB, extra=(), sources=SOURCES) -> list:
+    srcs = [os.path.join(CSRC, s) for s in sources]
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
         # keep the compiler from forming packed fp32 arithmetic in device code
@@ -36,17 +39,23 @@ def compile_command(out: str = LIB, extra=()) -> list:
     ]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile libfa.so; returns its path. Always recompiles."""
-    tmp = LIB + ".tmp"
-    cmd = compile_command(tmp, extra)
+def _compile(out: str, extra, sources, verbose: bool) -> str:
+    tmp = out + ".tmp"
+    cmd = compile_command(tmp, extra, sources)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + r.stdout + r.stderr)
     if verbose and r.stderr.strip():
         print(r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile libfa.so and the probe library; returns libfa.so's path.
+    Always recompiles."""
+    _compile(PROBE_LIB, (), PROBE_SOURCES, verbose)
+    return _compile(LIB, extra, SOURCES, verbose)
 
 
 if __name__ == "__main__":
