@@ -86,7 +86,9 @@ typedef enum {
   FA_ERR_ALIAS = 7,       /* an output or workspace overlaps an input or an output  */
   FA_ERR_OVERFLOW = 8,    /* the problem exceeds the kernel's index or grid range   */
                           /* (one head's bytes must stay below 2^31)               */
-  FA_ERR_HIP = 9          /* the HIP runtime refused a call; see fa_last_hip_error  */
+  FA_ERR_HIP = 9,         /* the HIP runtime refused a call; see fa_last_hip_error  */
+  FA_ERR_SCRATCH = 10     /* fa_forward_splitkv_noalloc: partials exceed its fixed
+                             scratch (fa_noalloc_scratch_bytes)                    */
 } fa_status;
 
 /*
@@ -190,6 +192,34 @@ int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, floa
 int fa_forward_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                        int batch, int heads, int n, int d_k, float scale, int causal, int dtype,
                        int splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_forward_splitkv_noalloc -- fa_forward_splitkv for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid allocation. Instead of a workspace argument, the
+ * per-block partials go to a fixed array of fa_noalloc_scratch_bytes()
+ * (128 MiB) that the library's code object holds on each GPU it runs on
+ * until the process ends. The call allocates nothing (no hipMalloc, no
+ * allocating library routine); the caller still passes q, k, v, o and lse.
+ * The result is that of fa_forward_splitkv with the same arguments, bit for
+ * bit (the same kernels on the same block count).
+ *
+ * The partials need fa_splitkv_workspace_size(batch, heads, n, d_k, splits)
+ * bytes; a call that needs more than the scratch returns FA_ERR_SCRATCH
+ * before any HIP call (use fa_forward_splitkv with a workspace then). Every
+ * call on one GPU uses that GPU's one scratch array: calls that overlap on
+ * one GPU (for instance on two streams at once) race on it and must be
+ * ordered by the caller. The array keeps the last call's partials; nothing
+ * in it needs to start at zero (every partial row is written before the
+ * merge reads it). Other arguments, status codes and the asynchronous
+ * contract as fa_forward_splitkv.
+ */
+int fa_forward_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int batch, int heads, int n, int d_k, float scale, int causal,
+                               int dtype, int splits, void* stream);
+
+/* Bytes of the fixed per-GPU scratch of fa_forward_splitkv_noalloc. */
+size_t fa_noalloc_scratch_bytes(void);
 
 /* Workspace bytes fa_forward_splitkv needs for these sizes; 0 when the keys
  * would not be split (or the sizes are invalid). Pure host computation. */

@@ -31,10 +31,11 @@ _OUT_DTYPE = {torch.float32: torch.float32, torch.float16: torch.float16,
 # fa_status (include/fa.h)
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_DTYPE",
           4: "FA_ERR_UNSUPPORTED", 5: "FA_ERR_ALIGN", 6: "FA_ERR_SCALE", 7: "FA_ERR_ALIAS",
-          8: "FA_ERR_OVERFLOW", 9: "FA_ERR_HIP"}
+          8: "FA_ERR_OVERFLOW", 9: "FA_ERR_HIP", 10: "FA_ERR_SCRATCH"}
 
 EXPORTS = ("fa_forward", "fa_forward_fp8", "fa_forward_strided", "fa_forward_varlen",
            "fa_forward_splitkv", "fa_splitkv_workspace_size", "fa_splitkv_splits",
+           "fa_forward_splitkv_noalloc", "fa_noalloc_scratch_bytes",
            "fa_backward", "fa_backward_workspace_size", "fa_backward_varlen", "fa_forward_unfused",
            "fa_unfused_workspace_size", "fa_status_string", "fa_last_hip_error",
            "fa_abi_version")
@@ -65,6 +66,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     sz = ctypes.c_size_t
     lib.fa_forward_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, vp, sz, vp]
     lib.fa_forward_splitkv.restype = i
+    lib.fa_forward_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, vp]
+    lib.fa_forward_splitkv_noalloc.restype = i
+    lib.fa_noalloc_scratch_bytes.argtypes = []
+    lib.fa_noalloc_scratch_bytes.restype = sz
     lib.fa_splitkv_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_splitkv_workspace_size.restype = sz
     lib.fa_splitkv_splits.argtypes = [i, i, i, i, i]
@@ -241,6 +246,31 @@ def forward_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, splits: O
     _check(st)
     return out, lse, workspace
 
+
+
+def forward_splitkv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, splits: Optional[int] = None,
+                            causal: bool = False, scale: Optional[float] = None,
+                            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """``fa_forward_splitkv_noalloc``: ``forward_splitkv`` with the per-block
+    partials in the library's fixed per-GPU scratch instead of a workspace
+    (for callers that cannot allocate; pass ``out`` and ``lse`` to allocate
+    nothing here either). Returns (O, LSE)."""
+    lib = load_library()
+    out, lse = _prepare(q, k, v, out, lse)
+    b, h, n, d = q.shape
+    if splits is None:
+        splits = splitkv_splits(b, h, n, causal)
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib.fa_forward_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, h, n, d, s,
+                                        1 if causal else 0, _DTYPE_CODE[q.dtype], int(splits),
+                                        _stream(q.device))
+    _check(st)
+    return out, lse
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the fixed per-GPU scratch of ``forward_splitkv_noalloc``."""
+    return int(load_library().fa_noalloc_scratch_bytes())
 
 
 def backward_workspace_size(batch: int, heads: int, n: int) -> int:

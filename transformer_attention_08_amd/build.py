@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ("fa_fwd.hip", "fa_bwd.hip", "fa_unfused.hip", "fa_api.cpp")
+SOURCES = ("fa_fwd.hip", "fa_bwd.hip", "fa_unfused.hip", "fa_noalloc.hip", "fa_api.cpp")
 # the matrix-core rate probe behind `bench.py --mfma-rate`; a library of its own
 PROBE_LIB = os.path.join(PKG, "libfa_probe.so")
 PROBE_SOURCES = ("fa_probe.hip",)

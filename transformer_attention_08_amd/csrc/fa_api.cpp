@@ -471,6 +471,29 @@ int fa_forward_splitkv(const void* q, const void* k, const void* v, void* o, flo
              workspace);
 }
 
+size_t fa_noalloc_scratch_bytes(void) { return fa::kNoallocScratchBytes; }
+
+int fa_forward_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int batch, int heads, int n, int d_k, float scale, int causal,
+                               int dtype, int splits, void* stream) {
+  const int st = validate(q, k, v, o, lse, batch, heads, n, d_k, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (splits < 1 || splits > kMaxSplits) return FA_ERR_UNSUPPORTED;
+  const int used = splits_used(n, splits);
+  const size_t need = used > 1 ? split_layout(batch, heads, n, d_k, used).total : 0;
+  if (need > fa::kNoallocScratchBytes) return FA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = fa::noalloc_scratch(&ws);
+    if (e != hipSuccess) {
+      g_last_hip_error = (int)e;
+      return FA_ERR_HIP;
+    }
+  }
+  return fa_forward_splitkv(q, k, v, o, lse, batch, heads, n, d_k, scale, causal, dtype, splits, ws, need,
+                            stream);
+}
+
 size_t fa_unfused_workspace_size(int batch, int heads, int n) {
   if (batch < 1 || heads < 1 || n < 1) return 0;
   if ((double)batch * heads * (double)n * n * 6.0 > 9.0e18) return 0;
@@ -597,6 +620,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_ALIAS: return "an output or workspace overlaps an input or another output";
     case FA_ERR_OVERFLOW: return "problem exceeds the kernel's index or grid range";
     case FA_ERR_HIP: return "HIP runtime error (see fa_last_hip_error)";
+    case FA_ERR_SCRATCH: return "split-KV partials exceed the fixed scratch of fa_forward_splitkv_noalloc (see fa_noalloc_scratch_bytes)";
     default: return "unknown status";
   }
 }

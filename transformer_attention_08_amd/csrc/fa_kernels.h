@@ -131,4 +131,9 @@ hipError_t launch_unfused(const UnfArgs& a, hipStream_t stream);
 // Compute units of the current device (256 on MI355X), read once per device.
 int device_cus();
 
+// Size of the fixed per-GPU scratch array of fa_forward_splitkv_noalloc, and
+// its device address on the current device (looked up once per device).
+constexpr size_t kNoallocScratchBytes = (size_t)128 << 20;
+hipError_t noalloc_scratch(void** out);
+
 }  // namespace fa
