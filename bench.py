@@ -22,6 +22,7 @@ that no input is served from the L2s or the 256 MB Infinity Cache
     python bench.py --copy-calibration      # plain copy of known size (counter scale)
     python bench.py --mfma-rate             # issue rate of the 32x32x16 and 16x16x32 MFMAs
     python bench.py --lds-rate              # LDS read bandwidth (16-byte and transposing reads)
+    python bench.py --coissue               # MFMA beside vector work, with register or LDS operands
 """
 from __future__ import annotations
 
@@ -245,6 +246,67 @@ def lds_rate(iters: int = 4000, blocks: int = 256):
                               "shader_ghz": round(ghz, 3)}), flush=True)
 
 
+def coissue(iters: int = 400, blocks: int = 256):
+    """MFMA / vector co-issue (the libfa_probe.so kernel): per CU, four waves
+    issue 32x32x16 MFMAs (operands from registers, from 16-byte LDS reads or
+    from transposing LDS reads) beside four waves running a softmax-like
+    vector stream, each pair on one SIMD; each alone and both together. One
+    JSON line per variant: shader cycles per MFMA of the matrix waves and per
+    64-score softmax of the vector waves."""
+    import ctypes
+
+    import torch
+
+    from transformer_attention_08_amd import build as _b
+
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    lib.fa_probe_coissue.restype = ctypes.c_int
+    lib.fa_probe_coissue.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 3
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(512, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    names = {0: "registers", 1: "ds_read_b128", 2: "2x ds_read_b64_tr_b16"}
+    for opnd in (0, 1, 2):
+        row = {"probe": "coissue", "mfma_operands": names[opnd]}
+        for role, tag in ((1, "matrix_alone"), (2, "vector_alone"), (3, "both")):
+            out = torch.zeros(8 * blocks, dtype=torch.int64, device=dev)
+            for _ in range(2):
+                rc = lib.fa_probe_coissue(opnd, role, blocks, iters, out.data_ptr(), sink.data_ptr(),
+                                          stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"probe launch failed: hipError {rc}")
+                torch.cuda.synchronize(dev)
+            cyc = out.double().cpu().view(blocks, 8)
+            if role & 1:
+                row[tag + "_cycles_per_mfma"] = round(float(cyc[:, :4].max(dim=1).values.median()) / (32 * iters), 2)
+            if role & 2:
+                row[tag + "_cycles_per_softmax"] = round(float(cyc[:, 4:].max(dim=1).values.median()) / iters, 1)
+        print(json.dumps(row), flush=True)
+
+
+def wave_placement(blocks: int = 4):
+    """SIMD of each wave of 512-thread workgroups (HW_ID register), per workgroup."""
+    import ctypes
+
+    import torch
+
+    from transformer_attention_08_amd import build as _b
+
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    lib.fa_probe_hwid.restype = ctypes.c_int
+    lib.fa_probe_hwid.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    out = torch.zeros(8 * blocks, dtype=torch.int32, device="cuda")
+    rc = lib.fa_probe_hwid(blocks, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"probe launch failed: hipError {rc}")
+    ids = [int(x) & 0xffffffff for x in out.cpu().tolist()]
+    for b in range(blocks):
+        w = ids[8 * b: 8 * b + 8]
+        print(json.dumps({"probe": "wave_placement", "workgroup": b,
+                          "simd_of_wave": [(x >> 4) & 3 for x in w], "wave_slot": [x & 15 for x in w],
+                          "cu": [(x >> 8) & 15 for x in w]}), flush=True)
+
+
 def backward_flops(w) -> float:
     """The five products of the gradient (S recomputed, dP, dV, dQ, dK), 2*n*n*d_k
     FLOP each per head; halved under a causal mask (2.5 x the forward count)."""
@@ -442,6 +504,8 @@ def main(argv=None):
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--mfma-rate", action="store_true",
                     help="issue rate of the 32x32x16 and 16x16x32 MFMAs (libfa_probe.so)")
+    ap.add_argument("--coissue", action="store_true",
+                    help="MFMA / vector co-issue with register or LDS operands (libfa_probe.so)")
     ap.add_argument("--lds-rate", action="store_true",
                     help="LDS read bandwidth of ds_read_b128 and ds_read_b64_tr_b16 (libfa_probe.so)")
     args = ap.parse_args(argv)
@@ -460,6 +524,10 @@ def main(argv=None):
         return 0
     if args.lds_rate:
         lds_rate()
+        return 0
+    if args.coissue:
+        coissue()
+        wave_placement()
         return 0
 
     import torch

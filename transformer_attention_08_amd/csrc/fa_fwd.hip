@@ -196,6 +196,9 @@ constexpr int kDirectBq = 32 * kDirectWaves;
 #ifndef FA_QK_AHEAD
 #define FA_QK_AHEAD 6
 #endif
+#ifndef FA_PV_AHEAD
+#define FA_PV_AHEAD 4
+#endif
 #ifndef FA_PAIR_TILES_NOMASK
 #define FA_PAIR_TILES_NOMASK 1
 #endif
@@ -231,6 +234,49 @@ __device__ inline void qk_tile(f32x16_t (&s)[KB], const uint8_t* k, int krow, in
 #else
 #pragma unroll
   for (int i = 0; i < NKS * KB; ++i) s[i % KB] = mfma16<IN>(*kaddr(i), qf[i / KB], s[i % KB]);
+#endif
+}
+
+// O^T += V^T P^T for one key tile: for each 32-key block kb, 16-key half s2
+// and 32-column block db, the V^T operand (eight consecutive keys at one
+// d-column per lane) comes from two transposing LDS reads of the swizzled V
+// tile, and P^T (packed 16-bit p) is the register-held B operand. With
+// FA_PV_AHEAD > 0 the V^T operands are read that many MFMAs ahead in a fixed
+// order, the read of operand i + FA_PV_AHEAD issued right after MFMA i, so
+// that the latency of the transposing reads hides behind the MFMAs already
+// issued.
+template <Elt IN, int KB, int NDB, int ROWB>
+__device__ inline void pv_tile(f32x16_t (&o)[NDB], const uint8_t* v, int vrow0, int vcol, int vswz,
+                               const u32x4_t (&pb)[KB][2]) {
+  auto vread = [&](int i) __attribute__((always_inline)) -> u32x4_t {
+    const int kb = i / (2 * NDB), s2 = (i / NDB) % 2, db = i % NDB;
+    const int row = kb * 32 + 16 * s2 + vrow0;
+    const int col = db * 32 + vcol;
+    const uint8_t* p0 = v + row * ROWB + (((col >> 3) ^ vswz) * 16) + ((col & 4) << 1);
+    const u32x2_t lo = lds_read_tr16(p0);
+    const u32x2_t hi = lds_read_tr16(p0 + 4 * ROWB);
+    return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+  };
+  constexpr int NPV = KB * 2 * NDB;
+#if FA_PV_AHEAD > 0
+  constexpr int PA = FA_PV_AHEAD < NPV ? FA_PV_AHEAD : NPV;
+  u32x4_t vf[PA];
+#pragma unroll
+  for (int i = 0; i < PA; ++i) vf[i] = vread(i);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) {
+    const int kb = i / (2 * NDB), s2 = (i / NDB) % 2, db = i % NDB;
+    o[db] = mfma16<IN>(vf[i % PA], pb[kb][s2], o[db]);
+    if (i + PA < NPV) vf[i % PA] = vread(i + PA);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#else
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) {
+    const int kb = i / (2 * NDB), s2 = (i / NDB) % 2, db = i % NDB;
+    o[db] = mfma16<IN>(vread(i), pb[kb][s2], o[db]);
+  }
 #endif
 }
 
@@ -405,21 +451,7 @@ void fwd_direct(FwdArgs a) {
     // the next tile's copies go out here, between the softmax and P.V (see step)
     mid();
     // O^T += V^T P^T; consecutive MFMAs go to different accumulators
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int row = kb * 32 + 16 * s2 + vrow0;
-          const int col = db * 32 + vcol;
-          const uint8_t* p0 = slot.v + row * ROWB + (((col >> 3) ^ vswz) * 16) + ((col & 4) << 1);
-          const u32x2_t lo = lds_read_tr16(p0);
-          const u32x2_t hi = lds_read_tr16(p0 + 4 * ROWB);
-          o[db] = mfma16<IN>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pb[kb][s2], o[db]);
-        }
-      }
-    }
+    pv_tile<IN, KB, NDB, ROWB>(o, slot.v, vrow0, vcol, vswz, pb);
   };
 
   auto slot_ref = [&](auto S) __attribute__((always_inline)) -> LdsSlot<TILE_B>& {
@@ -679,21 +711,7 @@ void fwd_direct8(FwdArgs a) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[db] *= alpha;
     }
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int row = kb * 32 + 16 * s2 + vrow0;
-          const int col = db * 32 + vcol;
-          const uint8_t* p0 = slot.v + row * ROWB + (((col >> 3) ^ vswz) * 16) + ((col & 4) << 1);
-          const u32x2_t lo = lds_read_tr16(p0);
-          const u32x2_t hi = lds_read_tr16(p0 + 4 * ROWB);
-          o[db] = mfma16<Elt::BF16>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pb[kb][s2], o[db]);
-        }
-      }
-    }
+    pv_tile<Elt::BF16, KB, NDB, ROWB>(o, slot.v, vrow0, vcol, vswz, pb);
   };
 
   // Step j: tile j is in `cur`; tile j + 1 is staged; tile j + 2 is copied next.
