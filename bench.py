@@ -20,6 +20,7 @@ that no input is served from the L2s or the 256 MB Infinity Cache
     python bench.py --layout bshd   # [batch, n, heads, d_k] inputs (fa_forward_strided)
     python bench.py --varlen 16     # a ragged batch of 16 sequences (fa_forward_varlen)
     python bench.py --copy-calibration      # plain copy of known size (counter scale)
+    python bench.py --traffic-record F W CF CW   # the stored HBM traffic record from counter files
     python bench.py --mfma-rate             # issue rate of the 32x32x16 and 16x16x32 MFMAs
     python bench.py --lds-rate              # LDS read bandwidth (16-byte and transposing reads)
     python bench.py --coissue               # MFMA beside vector work, with register or LDS operands
@@ -151,6 +152,58 @@ def cpu_baseline_backward(w, inp, do, budget_s: float = 15.0):
             "sample": f"{done} of {w.batch * w.heads} heads, all {w.n} rows each, fp64 NumPy "
                       f"(S, P, dP, dS materialised), {elapsed:.1f} s; the products run on {blas} BLAS "
                       f"threads, the exponentials on one thread"}
+
+
+def traffic_record(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out=TRAFFIC_FILE):
+    """Write the HBM traffic record of the forward at the Llama shape from four
+    rocprofv3 counter files: FETCH_SIZE and WRITE_SIZE of `bench.py --steps 3
+    --warmup 1 --no-cpu-baseline --no-cold-cache`, and the same two counters
+    of `bench.py --copy-calibration` (a 1 GiB device copy), which scale the
+    counters' KiB to bytes. The record carries the hash of the kernel sources
+    it was taken on; bench.py reports it only while the hash matches."""
+    import csv
+
+    def vals(path, kern):
+        rows = list(csv.DictReader(open(path)))
+        v = [float(r["Counter_Value"]) for r in rows if kern in r["Kernel_Name"]]
+        if not v:
+            raise RuntimeError(f"no {kern} dispatch in {path}")
+        return v
+
+    fv, wv = vals(fetch_csv, "fwd_direct"), vals(write_csv, "fwd_direct")
+    cfv, cwv = vals(copy_fetch_csv, "copyBuffer"), vals(copy_write_csv, "copyBuffer")
+    fetch, write = sum(fv) / len(fv), sum(wv) / len(wv)
+    cfk, cwk = sum(cfv) / len(cfv), sum(cwv) / len(cwv)
+    nb = 1 << 30
+    rf, wf = nb / (cfk * 1024), nb / (cwk * 1024)
+    rd, wr = fetch * 1024 * rf, write * 1024 * wf
+    import workload
+    mn = min_hbm_bytes(workload.WORKLOADS["llama3_8b_bf16_causal"])
+    bench_cmd = "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-cold-cache"
+    t = {
+        "kernel": "fwd_direct<bf16, d_k 128, causal>",
+        "workload": "llama3_8b_bf16_causal [1, 32, 8192, 128]",
+        "kernel_source_hash": kernel_source_hash(),
+        "kernel_sources": list(KERNEL_SOURCES),
+        "fetch_size_kib_per_dispatch": round(fetch, 1),
+        "write_size_kib_per_dispatch": round(write, 1),
+        "dispatches_counted": len(fv),
+        "copy_calibration": {"bytes_read": nb, "bytes_written": nb, "fetch_size_kib": round(cfk, 4),
+                             "write_size_kib": round(cwk, 4), "read_factor": rf, "write_factor": wf},
+        "hbm_read_bytes_per_launch": int(rd), "hbm_write_bytes_per_launch": int(wr),
+        "hbm_bytes_per_launch": int(rd + wr), "min_hbm_bytes": mn, "ratio_to_min": round((rd + wr) / mn, 2),
+        "commands": [
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o pmc -- {bench_cmd}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o pmc -- {bench_cmd}",
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o pmc -- python3 bench.py --copy-calibration",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o pmc -- python3 bench.py --copy-calibration",
+            "python3 bench.py --traffic-record <the four pmc_counter_collection.csv files, in that order>"],
+    }
+    with open(out, "w") as f:
+        json.dump(t, f, indent=1)
+        f.write("\n")
+    print(json.dumps({"traffic_record": out, "hbm_bytes_per_launch": t["hbm_bytes_per_launch"],
+                      "ratio_to_min": t["ratio_to_min"]}))
 
 
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
@@ -502,6 +555,9 @@ def main(argv=None):
     ap.add_argument("--no-cold-cache", action="store_true",
                     help="skip the second pass that reads 512 MiB of other device memory before each call")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--traffic-record", nargs=4, metavar="CSV",
+                    help="write the HBM traffic record from four rocprofv3 counter files "
+                         "(forward FETCH_SIZE, forward WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE)")
     ap.add_argument("--mfma-rate", action="store_true",
                     help="issue rate of the 32x32x16 and 16x16x32 MFMAs (libfa_probe.so)")
     ap.add_argument("--coissue", action="store_true",
@@ -518,6 +574,9 @@ def main(argv=None):
 
     if args.copy_calibration:
         copy_calibration()
+        return 0
+    if args.traffic_record:
+        traffic_record(*args.traffic_record)
         return 0
     if args.mfma_rate:
         mfma_rate()

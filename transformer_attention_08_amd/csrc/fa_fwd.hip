@@ -280,6 +280,37 @@ __device__ inline void pv_tile(f32x16_t (&o)[NDB], const uint8_t* v, int vrow0, 
 #endif
 }
 
+// Epilogue store of one wave's 32 rows of O through LDS. The O^T
+// accumulator holds one query row per lane, so storing it directly writes 32
+// rows, 16 bytes each, per store instruction; at the end of a query tile the
+// eight waves of every workgroup then queue 4096 such partial-line writes.
+// Here each lane first writes its row's packed values into the wave's
+// 32-row block of `stage` (16-byte chunks XOR-swizzled by row, conflict-free
+// in both directions), then reads the block back as 16-byte chunks of whole
+// rows, so that each store instruction writes four complete rows. Rows at or
+// past nrows are not stored.
+template <Elt IN, int NDB>
+__device__ inline void store_o_staged(uint8_t* stage, int lr, int hl, int lane, const f32x16_t (&o)[NDB],
+                                      float inv, uint16_t* orow0, size_t ors, int nrows) {
+  constexpr int ROWB = NDB * 32 * 2, CPR = ROWB / 16;  // bytes and 16-byte chunks per row
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int ch = db * 4 + g;  // the chunk of d-columns db*32 + 8g .. +7; this lane's half is hl
+      const uint32_t x0 = pack2<IN>(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+      const uint32_t x1 = pack2<IN>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+      *(u32x2_t*)(stage + lr * ROWB + ((ch ^ (lr % CPR)) * 16) + hl * 8) = u32x2_t{x0, x1};
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 32 * CPR / 64; ++k) {
+    const int c = k * 64 + lane, row = c / CPR, ch = c % CPR;
+    const u32x4_t x = *(const u32x4_t*)(stage + row * ROWB + ((ch ^ (row % CPR)) * 16));
+    if (row < nrows) *(u32x4_t*)(orow0 + (size_t)row * ors + ch * 8) = x;
+  }
+}
+
 template <int D>
 struct DirectLayout {
   // keys per tile (64 when a smaller tile would leave a wave without a load)
@@ -461,24 +492,19 @@ void fwd_direct(FwdArgs a) {
     else return ring3;
   };
   // Epilogue of a query tile: O = o / l once per row; LSE = ln 2 * (m2 + log2 l).
-  auto finish = [&]() __attribute__((always_inline)) {
+  // O goes out through `stage`, a ring slot no wave reads any more once every
+  // wave has passed the barrier here (the copies in flight fill the other
+  // slot).
+  auto finish = [&](uint8_t* stage) __attribute__((always_inline)) {
     const float lt = pair_sum(lp);
-    if (qrow < n && a.part_o) {
-      store_partial<NDB>(a, tl.bh, qrow, hl, o, m2, lt);
-    } else if (qrow < n) {
+    if (a.part_o) {
+      if (qrow < n) store_partial<NDB>(a, tl.bh, qrow, hl, o, m2, lt);
+    } else {
       const float inv = a.o_mult / lt;
-      uint16_t* Og = (uint16_t*)hv.o + (size_t)qrow * hv.ors;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = db * 32 + 8 * g + 4 * hl;
-          const uint32_t x0 = pack2<IN>(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
-          const uint32_t x1 = pack2<IN>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-          *(u32x2_t*)(Og + d) = u32x2_t{x0, x1};
-        }
-      }
-      if (hl == 0 && hv.lse) hv.lse[qrow] = (m2 + __log2f(lt)) * kLn2;
+      __syncthreads();
+      store_o_staged<IN, NDB>(stage + w * 32 * ROWB, lr, hl, lane, o, inv,
+                              (uint16_t*)hv.o + (size_t)qw0 * hv.ors, hv.ors, n - qw0);
+      if (qrow < n && hl == 0 && hv.lse) hv.lse[qrow] = (m2 + __log2f(lt)) * kLn2;
     }
   };
 
@@ -534,9 +560,10 @@ void fwd_direct(FwdArgs a) {
 
   run(j_lo, nt0, 0);
   if (pair) {
-    // the second query tile: its first keys are already in the ring; its Q
-    // loads land with them (the next step waits for both)
-    finish();
+    // the second query tile: its first keys are already in the ring (the
+    // slot of position nt0); its Q loads land with them (the next step waits
+    // for both). The slot of the first tile's last position is free for O.
+    finish(((nt0 - 1 - j_lo) & 1) ? (uint8_t*)&ring1 : (uint8_t*)&ring0);
     q0 = tl.t * kDirectBq;
     qw0 = q0 + 32 * w;
     qrow = qw0 + lr;
@@ -547,8 +574,8 @@ void fwd_direct(FwdArgs a) {
     for (int db = 0; db < NDB; ++db) o[db] = f32x16_t{};
     run(nt0, nt, nt0);
   }
-  wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
-  finish();
+  wait_vmcnt<0>();  // no load may still be writing LDS (nor may when the workgroup ends)
+  finish((uint8_t*)&ring0);
 }
 
 // ---------------------------------------------------------------------------
