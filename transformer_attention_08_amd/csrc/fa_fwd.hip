@@ -400,10 +400,10 @@ void fwd_direct(FwdArgs a) {
   // zeroed; loads complete in issue order, so the first step's wait for its
   // tile covers them too.
   u32x4_t qf[NKS];
-  auto load_q = [&]() __attribute__((always_inline)) {
+  auto load_q = [&](int row) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-      qf[ks] = bload16(rq, (uint32_t)qrow * hv.qrs + (ks * 16 + hl * 8) * 2);
+      qf[ks] = bload16(rq, (uint32_t)row * hv.qrs + (ks * 16 + hl * 8) * 2);
     // a negative scale: q -> -q (the sign bits; uniform branch, so the loads
     // are waited for here only in that case)
     if (a.qneg) {
@@ -411,7 +411,7 @@ void fwd_direct(FwdArgs a) {
       for (int ks = 0; ks < NKS; ++ks) qf[ks] ^= 0x80008000u;
     }
   };
-  load_q();
+  load_q(qrow);
 
   // Per-lane LDS read offsets.
   const int krow = perm32(lr);
@@ -561,13 +561,15 @@ void fwd_direct(FwdArgs a) {
   run(j_lo, nt0, 0);
   if (pair) {
     // the second query tile: its first keys are already in the ring (the
-    // slot of position nt0); its Q loads land with them (the next step waits
-    // for both). The slot of the first tile's last position is free for O.
+    // slot of position nt0). Its Q loads go out before the first tile's
+    // epilogue (the first tile no longer needs its Q fragments), so that
+    // their latency overlaps it; the next step waits for them and the keys.
+    // The slot of the first tile's last position is free for O.
+    load_q(tl.t * kDirectBq + 32 * w + lr);
     finish(((nt0 - 1 - j_lo) & 1) ? (uint8_t*)&ring1 : (uint8_t*)&ring0);
     q0 = tl.t * kDirectBq;
     qw0 = q0 + 32 * w;
     qrow = qw0 + lr;
-    load_q();
     m2 = -INFINITY;
     lp = 0.f;
 #pragma unroll
