@@ -24,6 +24,8 @@ that no input is served from the L2s or the 256 MB Infinity Cache
     python bench.py --mfma-rate             # issue rate of the 32x32x16 and 16x16x32 MFMAs
     python bench.py --lds-rate              # LDS read bandwidth (16-byte and transposing reads)
     python bench.py --coissue               # MFMA beside vector work, with register or LDS operands
+    python bench.py --valu-rate             # vector ALU rates: exp, fma, add, pack, max3, alone and paired
+    python bench.py --copy-rate             # global -> LDS copies, straight or through registers
 """
 from __future__ import annotations
 
@@ -337,6 +339,90 @@ def coissue(iters: int = 400, blocks: int = 256):
         print(json.dumps(row), flush=True)
 
 
+def valu_rate(iters: int = 2000, blocks: int = 256):
+    """Vector ALU issue rates (the libfa_probe.so kernel): per CU, waves 0-3
+    (one per SIMD) run operation A and waves 4-7 (their SIMD partners)
+    operation B, 16 independent instructions per round. One JSON line per
+    pair: shader cycles per instruction of each group (slowest wave of each
+    workgroup, median over workgroups)."""
+    import ctypes
+
+    import torch
+
+    from transformer_attention_08_amd import build as _b
+
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    lib.fa_probe_valu_rate.restype = ctypes.c_int
+    lib.fa_probe_valu_rate.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 3
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(512, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    names = {0: "idle", 1: "v_exp_f32", 2: "v_fma_f32", 3: "v_add_f32", 4: "v_cvt_pk_bf16_f32",
+             5: "v_max3_f32", 6: "v_exp_f16", 7: "mfma_32x32x16_bf16"}
+    pairs = [(1, 0), (2, 0), (3, 0), (4, 0), (5, 0), (6, 0), (7, 0), (1, 1), (2, 2), (1, 2), (1, 3), (7, 1), (7, 2)]
+    for op_a, op_b in pairs:
+        out = torch.zeros(8 * blocks, dtype=torch.int64, device=dev)
+        for _ in range(2):
+            rc = lib.fa_probe_valu_rate(op_a, op_b, blocks, iters, out.data_ptr(), sink.data_ptr(), stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed: hipError {rc}")
+            torch.cuda.synchronize(dev)
+        cyc = out.double().cpu().view(blocks, 8)
+        # an MFMA round issues 8 MFMAs, a vector round 16 instructions
+        per = {op: (8 if op == 7 else 16) * iters for op in (op_a, op_b)}
+        row = {"probe": "valu_rate", "waves_0_3": names[op_a], "waves_4_7": names[op_b],
+               "cycles_per_instr_0_3": round(float(cyc[:, :4].max(dim=1).values.median()) / per[op_a], 2)}
+        if op_b:
+            row["cycles_per_instr_4_7"] = round(float(cyc[:, 4:].max(dim=1).values.median()) / per[op_b], 2)
+        print(json.dumps(row), flush=True)
+
+
+def copy_rate(iters: int = 2000, blocks: int = 256):
+    """Global -> LDS copies (the libfa_probe.so kernel): bytes per cycle per
+    CU moved straight into LDS (buffer_load ... lds) or through registers,
+    alone and beside a stream of 16-byte LDS reads, from a 2 MiB source
+    (L2-resident) and from a 1 GiB one."""
+    import ctypes
+
+    import torch
+
+    from transformer_attention_08_amd import build as _b
+
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    lib.fa_probe_copy_rate.restype = ctypes.c_int
+    lib.fa_probe_copy_rate.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(512, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    names = {0: "lds_dma x8 waves", 1: "via registers x8 waves", 2: "lds_dma x4 + reads x4",
+             3: "via registers x4 + reads x4", 4: "reads x4 alone"}
+    for src_mib in (2, 1024):
+        src = torch.zeros(src_mib << 20, dtype=torch.uint8, device=dev)
+        for mode in range(5):
+            out = torch.zeros(16 * blocks, dtype=torch.int64, device=dev)
+            for _ in range(2):
+                rc = lib.fa_probe_copy_rate(mode, src.data_ptr(), src.numel(), blocks, iters, out.data_ptr(),
+                                            sink.data_ptr(), stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"probe launch failed: hipError {rc}")
+                torch.cuda.synchronize(dev)
+            v = out.view(blocks, 8, 2).double().cpu()
+            cyc, rounds = v[..., 0], v[..., 1]
+            row = {"probe": "copy_rate", "src_mib": src_mib, "mode": names[mode]}
+            copiers = list(range(8)) if mode <= 1 else list(range(4)) if mode <= 3 else []
+            readers = list(range(4, 8)) if mode >= 2 else []
+            if copiers:
+                t = cyc[:, copiers].max(dim=1).values
+                row["copy_bytes_per_clk_per_cu"] = round(float((len(copiers) * 4096 * iters / t).median()), 1)
+            if readers:
+                t = cyc[:, readers].max(dim=1).values
+                b = (rounds[:, readers] * 8 * 1024).sum(dim=1)
+                row["read_bytes_per_clk_per_cu"] = round(float((b / t).median()), 1)
+            print(json.dumps(row), flush=True)
+        del src
+
+
 def wave_placement(blocks: int = 4):
     """SIMD of each wave of 512-thread workgroups (HW_ID register), per workgroup."""
     import ctypes
@@ -560,6 +646,10 @@ def main(argv=None):
                          "(forward FETCH_SIZE, forward WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE)")
     ap.add_argument("--mfma-rate", action="store_true",
                     help="issue rate of the 32x32x16 and 16x16x32 MFMAs (libfa_probe.so)")
+    ap.add_argument("--copy-rate", action="store_true",
+                    help="global -> LDS copy rates, straight or through registers, beside LDS reads")
+    ap.add_argument("--valu-rate", action="store_true",
+                    help="vector ALU issue rates (exp, fma, add, pack, max3) alone and beside each other")
     ap.add_argument("--coissue", action="store_true",
                     help="MFMA / vector co-issue with register or LDS operands (libfa_probe.so)")
     ap.add_argument("--lds-rate", action="store_true",
@@ -583,6 +673,12 @@ def main(argv=None):
         return 0
     if args.lds_rate:
         lds_rate()
+        return 0
+    if args.valu_rate:
+        valu_rate()
+        return 0
+    if args.copy_rate:
+        copy_rate()
         return 0
     if args.coissue:
         coissue()

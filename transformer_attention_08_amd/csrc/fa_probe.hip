@@ -240,6 +240,203 @@ __global__ __launch_bounds__(512) void coissue(uint64_t* out, float* sink, int i
   if (sres == 12345.f) sink[threadIdx.x] = sres;
 }
 
+// Scores of e4m3 attention inputs on the two matrix paths an e4m3 kernel
+// could take: v_mfma_f32_32x32x16_fp8_fp8 on the codes themselves, and
+// v_mfma_f32_32x32x16_bf16 on the codes widened exactly to bf16 (every e4m3
+// value is a bf16 value). One wave per 32 x 32 block of S = Q K^T (raw
+// scores, before any scale), queries [0, rows) against all n keys of one
+// head; q8 and k8 are row-major e4m3 [n][128]. out8 / out16 are fp32
+// [rows][n].
+__global__ __launch_bounds__(64) void fp8_scores(const uint8_t* q8, const uint8_t* k8, int n, float* out8,
+                                                float* out16) {
+  const int lane = threadIdx.x, lr = lane & 31, hl = lane >> 5;
+  const int q0 = blockIdx.y * 32, k0 = blockIdx.x * 32;
+  f32x16_t2 s8 = {}, s16 = {};
+  for (int ks = 0; ks < 8; ++ks) {
+    const int dcol = ks * 16 + hl * 8;
+    const uint64_t a = *(const uint64_t*)(k8 + (size_t)(k0 + lr) * 128 + dcol);  // key k0 + lr
+    const uint64_t b = *(const uint64_t*)(q8 + (size_t)(q0 + lr) * 128 + dcol);  // query q0 + lr
+    s8 = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8((long)a, (long)b, s8, 0, 0, 0);
+    const uint32_t alo = (uint32_t)a, ahi = (uint32_t)(a >> 32), blo = (uint32_t)b, bhi = (uint32_t)(b >> 32);
+    u32x4_t aw = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(alo, 1.0f, false)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(alo, 1.0f, true)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ahi, 1.0f, false)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ahi, 1.0f, true))};
+    u32x4_t bw = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(blo, 1.0f, false)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(blo, 1.0f, true)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(bhi, 1.0f, false)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(bhi, 1.0f, true))};
+    s16 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, aw), __builtin_bit_cast(bf16x8_t, bw),
+                                                 s16, 0, 0, 0);
+  }
+  // accumulator register i of lane (lr, hl): key k0 + 8 (i / 4) + 4 hl + i % 4, query q0 + lr
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int key = k0 + 8 * (i / 4) + 4 * hl + (i % 4);
+    const size_t at = (size_t)(q0 + lr) * n + key;
+    out8[at] = s8[i];
+    out16[at] = s16[i];
+  }
+}
+
+// Global -> LDS copy rate, and how copies share the LDS with operand reads.
+// One workgroup of eight waves per CU (96 KiB of LDS). A copying wave moves
+// 4 KiB per round from src (offsets cycle through src_bytes, a power of two
+// of at least 64 KiB) into a double-buffered LDS area:
+//   MODE 0: all eight waves copy straight into LDS (buffer_load_dwordx4 ... lds);
+//   MODE 1: all eight waves copy through registers (16-byte buffer loads,
+//           then ds_write_b128), two rounds of registers in flight;
+//   MODE 2: waves 0-3 copy as in MODE 0 while waves 4-7 read LDS
+//           (eight ds_read_b128 per round) until the copies are done;
+//   MODE 3: as MODE 2 with MODE 1's copies;
+//   MODE 4: waves 4-7 read LDS alone (for as many rounds as in MODE 2).
+// out holds, per wave, its elapsed shader cycles and its rounds.
+__device__ inline void probe_dma16(__amdgpu_buffer_rsrc_t rsrc, uint8_t* lds, uint32_t voffset) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voffset), "s"(rsrc), "{m0}"(m0) : "memory");
+}
+
+template <int MODE>
+__global__ __launch_bounds__(512) void copy_rate(const uint8_t* src, uint32_t src_bytes, uint64_t* out, float* sink,
+                                                 int iters) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+  __shared__ int done;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src), (short)0, (int)src_bytes, 0x00020000);
+  for (int i = threadIdx.x * 16; i < kLdsBytes; i += blockDim.x * 16) *(u32x4_t*)(lds + i) = u32x4_t{1u, 2u, 3u, 4u};
+  if (threadIdx.x == 0) done = 0;
+  __syncthreads();
+  const bool copier = MODE <= 1 || (MODE <= 3 && wave < 4);
+  const bool reader = MODE >= 2 && wave >= 4;
+  const int cw = MODE <= 1 ? wave : (wave & 3);        // copier slot
+  const int ncw = MODE <= 1 ? 8 : 4;                   // copying waves
+  int rounds = 0;
+  float acc = 0.f;
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  if (copier) {
+    auto off = [&](int it, int i) { return (((uint32_t)(it * ncw + cw) * 4096u) & (src_bytes - 1)) + i * 1024 + lane * 16; };
+    auto dst = [&](int it, int i) { return lds + (it & 1) * (ncw * 4096) + cw * 4096 + i * 1024; };
+    if constexpr (MODE == 0 || MODE == 2) {
+      for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) probe_dma16(rsrc, dst(it, i), off(it, i));
+        __builtin_amdgcn_s_waitcnt((4 & 15) | (7 << 4) | (15 << 8));  // vmcnt(4): one round in flight
+      }
+    } else {
+      u32x4_t ra[4], rb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        ra[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off(0, i), 0, 0));
+      for (int it = 0; it + 1 < iters; it += 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          rb[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off(it + 1, i), 0, 0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(u32x4_t*)(dst(it, i) + lane * 16) = ra[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ra[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off(it + 2, i), 0, 0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(u32x4_t*)(dst(it + 1, i) + lane * 16) = rb[i];
+      }
+    }
+    rounds = iters;
+    __builtin_amdgcn_s_waitcnt(0);
+    acc = __uint_as_float(*(const uint32_t*)(lds + (threadIdx.x * 4100) % kLdsBytes));  // keeps the copies
+    if (MODE >= 2 && lane == 0) __hip_atomic_fetch_add(&done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  } else if (reader) {
+    const int cap = MODE == 4 ? iters : 64 * iters;
+    u32x4_t x = {};
+    for (int it = 0; it < cap; ++it) {
+      u32x4_t r[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r[u] = *(const u32x4_t*)(lds + ((it * 8 + u) * 1024 + (wave & 3) * 16384 + lane * 16) % kLdsBytes);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x ^= r[u];
+      ++rounds;
+      if (MODE != 4 && (it & 7) == 7 && __hip_atomic_load(&done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 4) break;
+    }
+    acc = (float)(x[0] ^ x[1] ^ x[2] ^ x[3]);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  const uint64_t c1 = __builtin_amdgcn_s_memtime();
+  const int gw = blockIdx.x * 8 + wave;
+  if (lane == 0) {
+    out[2 * gw] = c1 - c0;
+    out[2 * gw + 1] = (uint64_t)rounds;
+  }
+  if (acc == 12345.f) sink[threadIdx.x] = acc;
+}
+
+// Vector ALU rate. Waves 0-3 (one per SIMD) run operation A, waves 4-7 (the
+// SIMD partners of waves 0-3) run operation B; 0 = idle, 1 = v_exp_f32,
+// 2 = v_fma_f32, 3 = v_add_f32, 4 = v_cvt_pk_bf16_f32, 5 = v_max3_f32,
+// 6 = v_exp_f16, 7 = v_mfma_f32_32x32x16_bf16 (four accumulators). Each
+// round issues 16 independent instructions (no result feeds a source in the
+// same round) and each wave records its elapsed shader cycles.
+template <int OP>
+__device__ inline float valu_round(float (&x)[16], const float (&y)[16], f32x16_t (&acc)[4], bf16x8_t a) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if constexpr (OP == 1) asm volatile("v_exp_f32 %0, %1" : "=v"(x[i]) : "v"(y[i]));
+    else if constexpr (OP == 2) asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(x[i]) : "v"(y[i]), "v"(y[(i + 1) & 15]));
+    else if constexpr (OP == 3) asm volatile("v_add_f32 %0, %1, %2" : "=v"(x[i]) : "v"(y[i]), "v"(y[(i + 1) & 15]));
+    else if constexpr (OP == 4) asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(x[i]) : "v"(y[i]), "v"(y[(i + 1) & 15]));
+    else if constexpr (OP == 5) asm volatile("v_max3_f32 %0, %1, %2, %0" : "+v"(x[i]) : "v"(y[i]), "v"(y[(i + 1) & 15]));
+    else if constexpr (OP == 6) asm volatile("v_exp_f16 %0, %1" : "=v"(x[i]) : "v"(y[i]));
+    else if constexpr (OP == 7) {
+      if ((i & 1) == 0) acc[(i >> 1) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, acc[(i >> 1) & 3], 0, 0, 0);
+    }
+  }
+  float r = 0.f;
+  if constexpr (OP >= 1 && OP <= 6) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("" ::"v"(x[i]));
+  }
+  return r;
+}
+
+template <int OP>
+__device__ inline void valu_run(int iters, float* sink, uint64_t* out, int gw, int lane) {
+  float x[16], y[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { y[i] = 0.01f * (float)((lane + i) & 15) - 0.07f; x[i] = y[i]; }
+  bf16x8_t a;
+  for (int e = 0; e < 8; ++e) a[e] = (__bf16)(1.0f + 0.001f * (float)((lane + e) & 7));
+  f32x16_t acc[4] = {};
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) valu_round<OP>(x, y, acc, a);
+  __builtin_amdgcn_s_waitcnt(0);
+  const uint64_t c1 = __builtin_amdgcn_s_memtime();
+  float r = x[0] + acc[0][0] + acc[1][0] + acc[2][0] + acc[3][0];
+  if (lane == 0) out[gw] = c1 - c0;
+  if (r == 12345.f) sink[lane] = r;
+}
+
+__global__ __launch_bounds__(512) void valu_rate(uint64_t* out, float* sink, int iters, int op_a, int op_b) {
+  // one workgroup per CU: the workgroup asks for more than half of the LDS
+  __shared__ uint8_t lds[kLdsBytes];
+  for (int i = threadIdx.x; i < kLdsBytes; i += blockDim.x) lds[i] = (uint8_t)(i == iters);
+  __syncthreads();
+  if (lds[(threadIdx.x * 37) % kLdsBytes] == 7) sink[threadIdx.x] = 1.f;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = blockIdx.x * 8 + wave;
+  const int op = wave < 4 ? op_a : op_b;
+  switch (op) {
+    case 1: valu_run<1>(iters, sink, out, gw, lane); break;
+    case 2: valu_run<2>(iters, sink, out, gw, lane); break;
+    case 3: valu_run<3>(iters, sink, out, gw, lane); break;
+    case 4: valu_run<4>(iters, sink, out, gw, lane); break;
+    case 5: valu_run<5>(iters, sink, out, gw, lane); break;
+    case 6: valu_run<6>(iters, sink, out, gw, lane); break;
+    case 7: valu_run<7>(iters, sink, out, gw, lane); break;
+    default: if (lane == 0) out[gw] = 0; break;
+  }
+}
+
 // Wave placement: each wave of a 512-thread workgroup records the HW_ID
 // hardware register (SIMD, CU, shader array and engine it runs on).
 __global__ __launch_bounds__(512) void hwid(uint32_t* out) {
@@ -293,6 +490,42 @@ int fa_probe_coissue(int opnd, int role, int blocks, int iters, uint64_t* out, f
                 : opnd == 2 ? (const void*)&coissue<2> : nullptr;
   if (!f) return (int)hipErrorInvalidValue;
   return (int)hipLaunchKernel(f, dim3(blocks), dim3(512), args, 0, static_cast<hipStream_t>(stream));
+}
+
+// Launch the copy-rate probe: `blocks` workgroups of 8 waves; src holds
+// src_bytes (a power of two, at least 65536); out holds 2 uint64 per wave
+// (16 * blocks).
+int fa_probe_copy_rate(int mode, const void* src, unsigned src_bytes, int blocks, int iters, uint64_t* out,
+                       float* sink, void* stream) {
+  if (mode < 0 || mode > 4 || !src || src_bytes < 65536 || (src_bytes & (src_bytes - 1)) || blocks < 1 || iters < 2 ||
+      iters % 2 || !out || !sink)
+    return (int)hipErrorInvalidValue;
+  const uint8_t* s8 = static_cast<const uint8_t*>(src);
+  void* args[] = {&s8, &src_bytes, &out, &sink, &iters};
+  const void* f = mode == 0 ? (const void*)&copy_rate<0> : mode == 1 ? (const void*)&copy_rate<1>
+                : mode == 2 ? (const void*)&copy_rate<2> : mode == 3 ? (const void*)&copy_rate<3>
+                : (const void*)&copy_rate<4>;
+  return (int)hipLaunchKernel(f, dim3(blocks), dim3(512), args, 0, static_cast<hipStream_t>(stream));
+}
+
+// Launch the vector ALU rate probe: `blocks` workgroups of 8 waves; out
+// holds one uint64 of shader cycles per wave (8 * blocks); op codes as in
+// valu_rate (0-7).
+int fa_probe_valu_rate(int op_a, int op_b, int blocks, int iters, uint64_t* out, float* sink, void* stream) {
+  if (op_a < 0 || op_a > 7 || op_b < 0 || op_b > 7 || blocks < 1 || iters < 1 || !out || !sink)
+    return (int)hipErrorInvalidValue;
+  void* args[] = {&out, &sink, &iters, &op_a, &op_b};
+  return (int)hipLaunchKernel((const void*)&valu_rate, dim3(blocks), dim3(512), args, 0,
+                              static_cast<hipStream_t>(stream));
+}
+
+// Launch the e4m3 score probe: rows and n multiples of 32, d_k 128.
+int fa_probe_fp8_scores(const void* q8, const void* k8, int n, int rows, float* out8, float* out16, void* stream) {
+  if (!q8 || !k8 || !out8 || !out16 || n < 32 || rows < 32 || n % 32 || rows % 32 || rows > n)
+    return (int)hipErrorInvalidValue;
+  void* args[] = {&q8, &k8, &n, &out8, &out16};
+  return (int)hipLaunchKernel((const void*)&fp8_scores, dim3(n / 32, rows / 32), dim3(64), args, 0,
+                              static_cast<hipStream_t>(stream));
 }
 
 // Launch the placement probe: out holds one HW_ID word per wave (8 * blocks).
