@@ -72,12 +72,12 @@ def test_workload_full(name, seed):
 
 @pytest.mark.parametrize("name,seed", [
     ("llama3_8b_bf16_causal", 0), ("llama3_8b_bf16_causal", 1), ("llama3_8b_bf16_causal", 2),
-    ("long_ctx_bf16_causal", 0),
+    ("long_ctx_bf16_causal", 0), ("long_ctx_bf16_causal", 1), ("long_ctx_bf16_causal", 2),
     ("fp8_e4m3_nomask", 0), ("fp8_e4m3_nomask", 1), ("fp8_e4m3_nomask", 2),
 ])
 def test_workload_sampled_rows(name, seed):
     w = workload.WORKLOADS[name]
-    rows = workload.sample_rows(w.n, 256 if w.n > 8192 else 512, seed)
+    rows = workload.sample_rows(w.n, 1024 if w.n > 8192 else 512, seed)
     say(f"workload {name} seed={seed} ({len(rows)} sampled rows per head)")
     check(workload.workload_inputs(w, seed), w.causal, w.scale, rows=rows)
 
