@@ -454,20 +454,34 @@ def backward_flops(w) -> float:
 
 
 def time_steps(step, stream, steps, warmup):
+    """`warmup` untimed calls, then `steps` calls timed as one block: one
+    event before the first and one after the last, on the launch stream. An
+    event recorded between two calls leaves the GPU idle for ~6 us (measured
+    in kernel traces: back-to-back calls start with no gap), so per-call
+    events stay out of the timed block. The same number of calls then runs
+    again, each between two events of its own, for the per-call median and
+    minimum. Returns (ms per call of the timed block, per-call ms)."""
     import torch
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     print(f"# warmup done ({warmup} calls)", file=sys.stderr, flush=True)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    evs[0].record(stream)
-    for i in range(steps):
+    e0.record(stream)
+    for _ in range(steps):
         step()
-        evs[i + 1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
-    return evs[0].elapsed_time(evs[-1]) / steps, per
+    total_ms = e0.elapsed_time(e1)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in evs]
+    return total_ms / steps, per
 
 
 def scrub_read(scrub, acc):
@@ -740,22 +754,8 @@ def main(argv=None):
         else:
             fa.forward(d.q, d.k, d.v, causal=w.causal, scale=w.scale, out=o, lse=lse)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    print(f"# warmup done ({args.warmup} calls)", file=sys.stderr, flush=True)
-
     stream = torch.cuda.current_stream(dev)  # the stream fa_forward enqueues on
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    evs[0].record(stream)
-    for i in range(args.steps):
-        step()
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
-    total_ms = evs[0].elapsed_time(evs[-1])
-    ms = total_ms / args.steps
+    ms, per = time_steps(step, stream, args.steps, args.warmup)
 
     flops = algorithmic_flops(w)
     tflops = flops / (ms * 1e-3) / 1e12
