@@ -50,6 +50,10 @@ namespace {
 #ifndef FA_BWD_TILE
 #define FA_BWD_TILE 64
 #endif
+#ifndef FA_BWD_SDP_AHEAD
+#define FA_BWD_SDP_AHEAD 4
+#endif
+static_assert(FA_BWD_SDP_AHEAD >= 1, "operand read-ahead");
 constexpr int kBwdStages = FA_BWD_STAGES;
 static_assert(kBwdStages >= 2 && kBwdStages <= 4, "stages");
 
@@ -474,15 +478,28 @@ void bwd_dkdv(BwdArgs a) {
   };
 
   // S = Q K^T and dP = dO V^T of the 32-query block qb
+  // The row-wise operand reads run FA_BWD_SDP_AHEAD MFMAs ahead in a pinned
+  // order (operand i is Q (even i) or dO (odd i) at k-step i / 2): the wave
+  // is alone on its SIMD, so nothing else hides an LDS read that an MFMA
+  // waits on.
   auto sdp = [&](const QSlot<TILE_B>& slot, int qb, f32x16_t& s, f32x16_t& dp) __attribute__((always_inline)) {
     s = f32x16_t{};
     dp = f32x16_t{};
     const int row = qb * 32 + qr;
+    constexpr int NOP = 2 * NKS, PA = FA_BWD_SDP_AHEAD < NOP ? FA_BWD_SDP_AHEAD : NOP;
+    auto rd = [&](int i) __attribute__((always_inline)) {
+      const int at = row * ROWB + (((2 * (i >> 1) + hl) ^ sw_r) * 16);
+      return *(const u32x4_t*)(((i & 1) ? slot.g : slot.q) + at);
+    };
+    u32x4_t buf[PA];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int at = row * ROWB + (((2 * ks + hl) ^ sw_r) * 16);
-      s = mfma16<IN>(*(const u32x4_t*)(slot.q + at), kf[ks], s);
-      dp = mfma16<IN>(*(const u32x4_t*)(slot.g + at), vf[ks], dp);
+    for (int i = 0; i < PA; ++i) buf[i] = rd(i);
+#pragma unroll
+    for (int i = 0; i < NOP; ++i) {
+      if (i & 1) dp = mfma16<IN>(buf[i % PA], vf[i >> 1], dp);
+      else s = mfma16<IN>(buf[i % PA], kf[i >> 1], s);
+      if (i + PA < NOP) buf[i % PA] = rd(i + PA);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   // Per tile, the products of block qb + 1 are issued before the softmax of
