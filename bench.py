@@ -380,8 +380,9 @@ def valu_rate(iters: int = 2000, blocks: int = 256):
 def copy_rate(iters: int = 2000, blocks: int = 256):
     """Global -> LDS copies (the libfa_probe.so kernel): bytes per cycle per
     CU moved straight into LDS (buffer_load ... lds) or through registers,
-    alone and beside a stream of 16-byte LDS reads, from a 2 MiB source
-    (L2-resident) and from a 1 GiB one."""
+    alone and beside a stream of 16-byte LDS reads or beside MFMAs fed by
+    16-byte LDS reads, from a 2 MiB source (L2-resident) and from a 1 GiB
+    one."""
     import ctypes
 
     import torch
@@ -396,10 +397,11 @@ def copy_rate(iters: int = 2000, blocks: int = 256):
     sink = torch.zeros(512, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     names = {0: "lds_dma x8 waves", 1: "via registers x8 waves", 2: "lds_dma x4 + reads x4",
-             3: "via registers x4 + reads x4", 4: "reads x4 alone"}
+             3: "via registers x4 + reads x4", 4: "reads x4 alone", 5: "lds_dma x4 + MFMA x4 (LDS operands)",
+             6: "MFMA x4 (LDS operands) alone", 7: "via registers x4 + MFMA x4 (LDS operands)"}
     for src_mib in (2, 1024):
         src = torch.zeros(src_mib << 20, dtype=torch.uint8, device=dev)
-        for mode in range(5):
+        for mode in range(8):
             out = torch.zeros(16 * blocks, dtype=torch.int64, device=dev)
             for _ in range(2):
                 rc = lib.fa_probe_copy_rate(mode, src.data_ptr(), src.numel(), blocks, iters, out.data_ptr(),
@@ -410,8 +412,13 @@ def copy_rate(iters: int = 2000, blocks: int = 256):
             v = out.view(blocks, 8, 2).double().cpu()
             cyc, rounds = v[..., 0], v[..., 1]
             row = {"probe": "copy_rate", "src_mib": src_mib, "mode": names[mode]}
-            copiers = list(range(8)) if mode <= 1 else list(range(4)) if mode <= 3 else []
-            readers = list(range(4, 8)) if mode >= 2 else []
+            copiers = list(range(8)) if mode <= 1 else list(range(4)) if mode in (2, 3, 5, 7) else []
+            readers = list(range(4, 8)) if mode in (2, 3, 4) else []
+            matrix = list(range(4, 8)) if mode >= 5 else []
+            if matrix:
+                t = cyc[:, matrix].max(dim=1).values
+                r = rounds[:, matrix].min(dim=1).values
+                row["cycles_per_mfma"] = round(float((t / (r * 32)).median()), 2)
             if copiers:
                 t = cyc[:, copiers].max(dim=1).values
                 row["copy_bytes_per_clk_per_cu"] = round(float((len(copiers) * 4096 * iters / t).median()), 1)

@@ -289,7 +289,12 @@ __global__ __launch_bounds__(64) void fp8_scores(const uint8_t* q8, const uint8_
 //   MODE 2: waves 0-3 copy as in MODE 0 while waves 4-7 read LDS
 //           (eight ds_read_b128 per round) until the copies are done;
 //   MODE 3: as MODE 2 with MODE 1's copies;
-//   MODE 4: waves 4-7 read LDS alone (for as many rounds as in MODE 2).
+//   MODE 4: waves 4-7 read LDS alone (for as many rounds as in MODE 2);
+//   MODE 5: waves 0-3 copy as in MODE 0 while waves 4-7 issue 32x32x16 bf16
+//           MFMAs whose A operands are 16-byte LDS reads (six ahead, 32 per
+//           round) until the copies are done;
+//   MODE 6: those MFMA waves alone (`iters` rounds);
+//   MODE 7: as MODE 5 with MODE 1's copies.
 // out holds, per wave, its elapsed shader cycles and its rounds.
 __device__ inline void probe_dma16(__amdgpu_buffer_rsrc_t rsrc, uint8_t* lds, uint32_t voffset) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
@@ -308,8 +313,10 @@ __global__ __launch_bounds__(512) void copy_rate(const uint8_t* src, uint32_t sr
   for (int i = threadIdx.x * 16; i < kLdsBytes; i += blockDim.x * 16) *(u32x4_t*)(lds + i) = u32x4_t{1u, 2u, 3u, 4u};
   if (threadIdx.x == 0) done = 0;
   __syncthreads();
-  const bool copier = MODE <= 1 || (MODE <= 3 && wave < 4);
-  const bool reader = MODE >= 2 && wave >= 4;
+  const bool copier = MODE <= 1 || ((MODE <= 3 || MODE == 5 || MODE == 7) && wave < 4);
+  const bool reader = MODE >= 2 && MODE <= 4 && wave >= 4;
+  const bool matrix = MODE >= 5 && wave >= 4;
+  constexpr bool kRegCopy = MODE == 1 || MODE == 3 || MODE == 7;
   const int cw = MODE <= 1 ? wave : (wave & 3);        // copier slot
   const int ncw = MODE <= 1 ? 8 : 4;                   // copying waves
   int rounds = 0;
@@ -318,7 +325,7 @@ __global__ __launch_bounds__(512) void copy_rate(const uint8_t* src, uint32_t sr
   if (copier) {
     auto off = [&](int it, int i) { return (((uint32_t)(it * ncw + cw) * 4096u) & (src_bytes - 1)) + i * 1024 + lane * 16; };
     auto dst = [&](int it, int i) { return lds + (it & 1) * (ncw * 4096) + cw * 4096 + i * 1024; };
-    if constexpr (MODE == 0 || MODE == 2) {
+    if constexpr (!kRegCopy) {
       for (int it = 0; it < iters; ++it) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) probe_dma16(rsrc, dst(it, i), off(it, i));
@@ -346,6 +353,29 @@ __global__ __launch_bounds__(512) void copy_rate(const uint8_t* src, uint32_t sr
     __builtin_amdgcn_s_waitcnt(0);
     acc = __uint_as_float(*(const uint32_t*)(lds + (threadIdx.x * 4100) % kLdsBytes));  // keeps the copies
     if (MODE >= 2 && lane == 0) __hip_atomic_fetch_add(&done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  } else if (matrix) {
+    bf16x8_t bop;
+    for (int e = 0; e < 8; ++e) bop[e] = (__bf16)(0.5f - 0.001f * (float)((lane * 3 + e) & 7));
+    f32x16_t macc[4] = {};
+    const int cap = MODE == 6 ? iters : 64 * iters;
+    const uint8_t* abase = lds + 32768 + (wave & 3) * 8192;  // outside the copies' double buffer
+    auto rd = [&](int i) { return *(const u32x4_t*)(abase + ((i & 7) * 1024 + lane * 16)); };
+    for (int it = 0; it < cap; ++it) {
+      u32x4_t buf[6];
+#pragma unroll
+      for (int i = 0; i < 6; ++i) buf[i] = rd(i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        macc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, buf[i % 6]), bop, macc[i & 3], 0, 0, 0);
+        if (i + 6 < 32) buf[i % 6] = rd(i + 6);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      ++rounds;
+      if (MODE != 6 && __hip_atomic_load(&done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 4) break;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc += macc[k][0];
   } else if (reader) {
     const int cap = MODE == 4 ? iters : 64 * iters;
     u32x4_t x = {};
@@ -497,14 +527,15 @@ int fa_probe_coissue(int opnd, int role, int blocks, int iters, uint64_t* out, f
 // (16 * blocks).
 int fa_probe_copy_rate(int mode, const void* src, unsigned src_bytes, int blocks, int iters, uint64_t* out,
                        float* sink, void* stream) {
-  if (mode < 0 || mode > 4 || !src || src_bytes < 65536 || (src_bytes & (src_bytes - 1)) || blocks < 1 || iters < 2 ||
+  if (mode < 0 || mode > 7 || !src || src_bytes < 65536 || (src_bytes & (src_bytes - 1)) || blocks < 1 || iters < 2 ||
       iters % 2 || !out || !sink)
     return (int)hipErrorInvalidValue;
   const uint8_t* s8 = static_cast<const uint8_t*>(src);
   void* args[] = {&s8, &src_bytes, &out, &sink, &iters};
-  const void* f = mode == 0 ? (const void*)&copy_rate<0> : mode == 1 ? (const void*)&copy_rate<1>
-                : mode == 2 ? (const void*)&copy_rate<2> : mode == 3 ? (const void*)&copy_rate<3>
-                : (const void*)&copy_rate<4>;
+  const void* fs[8] = {(const void*)&copy_rate<0>, (const void*)&copy_rate<1>, (const void*)&copy_rate<2>,
+                       (const void*)&copy_rate<3>, (const void*)&copy_rate<4>, (const void*)&copy_rate<5>,
+                       (const void*)&copy_rate<6>, (const void*)&copy_rate<7>};
+  const void* f = fs[mode];
   return (int)hipLaunchKernel(f, dim3(blocks), dim3(512), args, 0, static_cast<hipStream_t>(stream));
 }
 
