@@ -311,10 +311,26 @@ __device__ inline void store_o_staged(uint8_t* stage, int lr, int hl, int lane, 
   }
 }
 
-template <int D>
+// Direct store of one lane's row of O (8-byte stores of 4 consecutive
+// d-columns: o[db][4g + r] is d-column db*32 + 8g + 4*hl + r), for ring
+// layouts whose slot cannot hold the staged rows of every wave.
+template <Elt IN, int NDB>
+__device__ inline void store_o_row(uint16_t* row_ptr, int hl, const f32x16_t (&o)[NDB], float inv) {
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t x0 = pack2<IN>(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+      const uint32_t x1 = pack2<IN>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+      *(u32x2_t*)(row_ptr + db * 32 + 8 * g + 4 * hl) = u32x2_t{x0, x1};
+    }
+  }
+}
+
+template <int D, int KEYS = FA_DIRECT_KEYS>
 struct DirectLayout {
   // keys per tile (64 when a smaller tile would leave a wave without a load)
-  static constexpr int BK = FA_DIRECT_KEYS * D * 2 >= 1024 * kDirectWaves ? FA_DIRECT_KEYS : 64;
+  static constexpr int BK = KEYS * D * 2 >= 1024 * kDirectWaves ? KEYS : 64;
   static constexpr int ROWB = D * 2;            // bytes per K or V row
   static constexpr int CPR = D / 8;             // 16-byte chunks per row
   static constexpr int TILE_B = BK * ROWB;      // bytes per K (or V) tile
@@ -501,9 +517,15 @@ void fwd_direct(FwdArgs a) {
       if (qrow < n) store_partial<NDB>(a, tl.bh, qrow, hl, o, m2, lt);
     } else {
       const float inv = a.o_mult / lt;
-      __syncthreads();
-      store_o_staged<IN, NDB>(stage + w * 32 * ROWB, lr, hl, lane, o, inv,
-                              (uint16_t*)hv.o + (size_t)qw0 * hv.ors, hv.ors, n - qw0);
+      // the staged rows of all waves must fit in one ring slot (64-key tiles
+      // at d_k 128 leave a 32 KiB slot for 64 KiB of rows: store directly)
+      if constexpr (sizeof(LdsSlot<TILE_B>) >= (size_t)kDirectWaves * 32 * ROWB) {
+        __syncthreads();
+        store_o_staged<IN, NDB>(stage + w * 32 * ROWB, lr, hl, lane, o, inv,
+                                (uint16_t*)hv.o + (size_t)qw0 * hv.ors, hv.ors, n - qw0);
+      } else {
+        if (qrow < n) store_o_row<IN, NDB>((uint16_t*)hv.o + (size_t)qrow * hv.ors, hl, o, inv);
+      }
       if (qrow < n && hl == 0 && hv.lse) hv.lse[qrow] = (m2 + __log2f(lt)) * kLn2;
     }
   };
@@ -593,14 +615,14 @@ void fwd_direct(FwdArgs a) {
 // ---------------------------------------------------------------------------
 template <int D>
 struct Stage8 {
-  __attribute__((aligned(1024))) uint8_t k[DirectLayout<D>::BK * D];
-  __attribute__((aligned(1024))) uint8_t v[DirectLayout<D>::BK * D];
+  __attribute__((aligned(1024))) uint8_t k[DirectLayout<D, 128>::BK * D];
+  __attribute__((aligned(1024))) uint8_t v[DirectLayout<D, 128>::BK * D];
 };
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kDirectThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_direct8(FwdArgs a) {
-  using L = DirectLayout<D>;
+  using L = DirectLayout<D, 128>;  // e4m3 staging copies need 128-key tiles
   constexpr int BK = L::BK, ROWB = L::ROWB, TILE_B = L::TILE_B;
   constexpr int KB = BK / 32, NKS = D / 16, NDB = D / 32;
   constexpr int STILE = BK * D;                         // bytes per staged e4m3 tile (K or V)
