@@ -12,8 +12,10 @@
 //      streams the K/V tiles like the forward and accumulates dQ in
 //      registers. It also computes D for its rows (from dO and O) and
 //      -LSE*log2(e), and leaves both in the caller's workspace.
-//   2. bwd_dkdv, key-major: one workgroup per (batch*head, 128 keys) streams
-//      the Q / dO tiles (with D and LSE) and accumulates dK and dV.
+//   2. bwd_dkdv2, key-major: one workgroup per (batch*head, 128 keys)
+//      streams the Q / dO tiles (with D and LSE) and accumulates dK and dV;
+//      the two products of each key run on two waves that share a SIMD
+//      (bwd_dkdv, one wave per key block, is the single-wave form).
 // Each pass owns its outputs, so no atomics and no second reduction: the
 // result is deterministic. The price is that S and dP are computed in both
 // passes (7 matrix products instead of the 5 the gradient needs).
@@ -49,6 +51,12 @@ namespace {
 #endif
 #ifndef FA_BWD_TILE
 #define FA_BWD_TILE 64
+#endif
+#ifndef FA_BWD_SPLIT
+#define FA_BWD_SPLIT 1
+#endif
+#ifndef FA_BWD_LAG
+#define FA_BWD_LAG 1
 #endif
 #ifndef FA_BWD_SDP_AHEAD
 #define FA_BWD_SDP_AHEAD 4
@@ -609,6 +617,315 @@ void bwd_dkdv(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pass 2 with the two products of each key split over two waves, so that two
+// waves share every SIMD (the single-wave pass above holds K, V, dK and dV in
+// one wave, ~400 registers, alone on its SIMD). Eight waves, 128 keys: waves
+// w and w + 4 (one SIMD) own keys 32 (w mod 4) .. + 31 of the workgroup.
+//   wave w     (K in registers): S = Q K^T, P = exp2(c S - LSE log2 e), P to
+//              LDS, then dV^T += dO^T P;
+//   wave w + 4 (V in registers): dP = dO V^T, then, with P from LDS,
+//              dS = P (dP - D) and dK^T += Q^T dS.
+// Two barriers per tile: the tile has landed; P is in LDS. Each phase puts
+// 16 MFMAs of each wave of a SIMD on its matrix pipe, beside the vector work
+// of one of them (the exponentials in the first, dS in the second). dS is
+// formed from P as rounded to the input type, the P that dV uses too.
+// ---------------------------------------------------------------------------
+constexpr int kKv2Waves = 8;
+constexpr int kKv2Threads = 64 * kKv2Waves;
+
+template <Elt E>
+__device__ inline void unpack2(uint32_t x, float& a, float& b) {
+  if constexpr (E == Elt::F16) {
+    const f16x2_t h = __builtin_bit_cast(f16x2_t, x);
+    a = (float)h[0];
+    b = (float)h[1];
+  } else {
+    a = __uint_as_float(x << 16);
+    b = __uint_as_float(x & 0xffff0000u);
+  }
+}
+
+template <Elt IN, int D, bool CAUSAL>
+__global__ __launch_bounds__(kKv2Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv2(BwdArgs a) {
+  constexpr int ROWB = D * 2, TILE_B = kKvBq * ROWB;
+  constexpr int LPW = TILE_B / 1024 / kKv2Waves;
+  constexpr int NS = kBwdStages;
+  constexpr int NKS = D / 16, NDB = D / 32;
+  constexpr int QB = kKvBq / 32;
+  constexpr int LOADS = 2 * LPW + 2;  // per wave per tile
+  static_assert(LPW >= 1, "tile too small for the wave count");
+  static_assert(kKvBk == 4 * 32, "four key blocks of 32 per workgroup");
+
+  __shared__ QSlot<TILE_B> ring0, ring1, ring2, ring3;
+  // P of the current tile: [register half][key block][query block][lane]
+  __shared__ u32x4_t pbuf[2][4][QB][64];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kblk = w & 3;
+  const int lane = tid & 63, lr = lane & 31, hl = lane >> 5;
+  const int ktiles = (a.n + kKvBk - 1) / kKvBk;
+  const TileId tl = tile_of_block(blockIdx.x, a.bh, ktiles, false, kKvBk);
+  const BwdView hv = bwd_view(a, tl.bh);
+  const int n = hv.n;
+  const int k0 = tl.t * kKvBk;
+  if (k0 >= n) return;  // a tile past a short sequence (uniform)
+  const int kw0 = k0 + 32 * kblk;
+  const int key = kw0 + lr;
+  const uint32_t span = span_bytes(n, hv.rs, ROWB);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(hv.q, span);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(hv.g, span);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(hv.nlse2, (uint32_t)n * 4);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(hv.delta, (uint32_t)n * 4);
+
+  const int i_lo = CAUSAL ? k0 / kKvBq : 0;  // query tiles i_lo .. nt-1
+  const int nt = (n + kKvBq - 1) / kKvBq;
+
+  uint32_t off[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int byte = (w * LPW + i) * 1024 + lane * 16;
+    const int row = byte / ROWB, p = (byte % ROWB) / 16;
+    off[i] = (uint32_t)row * hv.rs + (uint32_t)((p ^ swz2<D>(row)) * 16);
+  }
+  auto issue = [&](QSlot<TILE_B>& slot, int t) __attribute__((always_inline)) {
+    const bool in = t < nt;
+    const uint32_t base = in ? (uint32_t)(t * kKvBq) * hv.rs : 0x80000000u;
+    const uint32_t sbase = in ? (uint32_t)t * (kKvBq * 4) : 0x80000000u;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      lds_dma16(rq, slot.q + (w * LPW + i) * 1024, base + off[i]);
+      lds_dma16(rg, slot.g + (w * LPW + i) * 1024, base + off[i]);
+    }
+    lds_dma16(rl, (uint8_t*)slot.st, sbase + lane * 16);
+    lds_dma16(rd, (uint8_t*)(slot.st + 256), sbase + lane * 16);
+  };
+
+  const int qr = perm32(lr);
+  const int sw_r = swz2<D>(qr);
+  const int grp = lane >> 4, li = lane & 15;
+  const int trow = 8 * hl + (li >> 2);
+  const int sw_lo = swz2<D>(trow), sw_hi = swz2<D>(trow + 4);
+  const int tcol = 16 * (grp & 1) + 4 * (li & 3);
+
+  const float c = a.c;
+  const float s_masked = c > 0.f ? -INFINITY : INFINITY;  // c * s_masked = -inf
+  const bool wave_live = kw0 < n;
+  auto live = [&](int i) __attribute__((always_inline)) {
+    return wave_live && !(CAUSAL && i * kKvBq + kKvBq - 1 < kw0);
+  };
+  auto needs_mask = [&](int i) __attribute__((always_inline)) {
+    return (kw0 + 31 >= n) || (CAUSAL && i * kKvBq < kw0 + 31);
+  };
+
+  // acc[qb] = X F^T for the 32-row query blocks qb of X (Q or dO) and this
+  // lane's key fragments F (K or V). The MFMAs alternate between the blocks
+  // (two independent accumulators); operand i (block i % QB, k-step i / QB)
+  // is read FA_BWD_SDP_AHEAD MFMAs ahead in a pinned order.
+  auto prod = [&](const uint8_t* x, const u32x4_t (&f)[NKS], f32x16_t (&acc)[QB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) acc[qb] = f32x16_t{};
+    constexpr int NOP = QB * NKS, PA = FA_BWD_SDP_AHEAD < NOP ? FA_BWD_SDP_AHEAD : NOP;
+    auto rd_ = [&](int i) __attribute__((always_inline)) {
+      const int row = (i % QB) * 32 + qr, ks = i / QB;
+      return *(const u32x4_t*)(x + row * ROWB + (((2 * ks + hl) ^ sw_r) * 16));
+    };
+    u32x4_t buf[PA];
+#pragma unroll
+    for (int i = 0; i < PA; ++i) buf[i] = rd_(i);
+#pragma unroll
+    for (int i = 0; i < NOP; ++i) {
+      acc[i % QB] = mfma16<IN>(buf[i % PA], f[i / QB], acc[i % QB]);
+      if (i + PA < NOP) buf[i % PA] = rd_(i + PA);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // acc[db] += X^T B over the 32 queries of block qb: X^T (dO^T or Q^T) from
+  // transposing reads, B (P or dS, 16 queries per half) from registers.
+  auto prod_t = [&](const uint8_t* x, int qb, const u32x4_t (&b)[2], f32x16_t (&acc)[NDB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int r = qb * 32 + 16 * s2 + trow;
+        const int col = db * 32 + tcol;
+        const int half = (col & 4) << 1;
+        const u32x2_t lo = lds_read_tr16(x + r * ROWB + (((col >> 3) ^ sw_lo) * 16) + half);
+        const u32x2_t hi = lds_read_tr16(x + (r + 4) * ROWB + (((col >> 3) ^ sw_hi) * 16) + half);
+        acc[db] = mfma16<IN>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, b[s2], acc[db]);
+      }
+    }
+  };
+
+  auto slot_ref = [&](auto S) __attribute__((always_inline)) -> QSlot<TILE_B>& {
+    if constexpr (decltype(S)::value == 0) return ring0;
+    else if constexpr (decltype(S)::value == 1) return ring1;
+    else if constexpr (decltype(S)::value == 2) return ring2;
+    else return ring3;
+  };
+
+  // The two roles run separate copies of the tile loop with the same
+  // sequence of barriers, so each keeps only its own registers.
+  auto run = [&](auto ROLE) __attribute__((always_inline)) {
+    constexpr bool kS = decltype(ROLE)::value;  // the S / P / dV wave
+    u32x4_t f[NKS];  // K (kS) or V of this lane's key, d-columns ks*16 + hl*8 .. +8
+    {
+      const __amdgpu_buffer_rsrc_t rf = make_rsrc(kS ? hv.k : hv.v, span);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) f[ks] = bload16(rf, (uint32_t)key * hv.rs + (ks * 16 + hl * 8) * 2);
+    }
+    wait_vmcnt<0>();
+    f32x16_t acc[NDB];  // dV (kS) or dK
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
+
+    {
+      QSlot<TILE_B>* slots[4] = {&ring0, &ring1, &ring2, &ring3};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        u32x4_t* p = (u32x4_t*)slots[s];
+        for (int i = tid; i < (int)(sizeof(QSlot<TILE_B>) / 16); i += kKv2Threads) p[i] = u32x4_t{0, 0, 0, 0};
+      }
+    }
+    __syncthreads();
+    issue(ring0, i_lo);
+    if constexpr (NS > 2) issue(ring1, i_lo + 1);
+    if constexpr (NS > 3) issue(ring2, i_lo + 2);
+
+    // dS of the previous tile and whether that tile was live (dS waves): its
+    // dK product runs in the next step, beside the S waves' exponentials.
+    u32x4_t dsp[QB][2];
+    bool pl = false;
+    auto step = [&](auto S, int it) __attribute__((always_inline)) {
+      using SN = std::integral_constant<int, (decltype(S)::value + NS - 1) % NS>;
+      wait_vmcnt<(NS - 2) * LOADS>();
+      __syncthreads();  // tile it has landed; every wave is past tile it - 1
+#if !FA_BWD_LAG
+      issue(slot_ref(SN{}), it + NS - 1);
+#endif
+      const QSlot<TILE_B>& slot = slot_ref(S);
+      const bool lv = live(it);
+      if constexpr (kS) {
+        u32x4_t pb[QB][2];
+        if (lv) {
+          f32x16_t sv[QB];
+          prod(slot.q, f, sv);
+          const bool mask = needs_mask(it);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            // register r holds query qb*32 + 16*(r >> 3) + 8*hl + (r & 7)
+            float nl[16];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                const u32x4_t x = *(const u32x4_t*)(slot.st + qb * 32 + 16 * h + 8 * hl + 4 * e);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) nl[8 * h + 4 * e + r] = __uint_as_float(x[r]);
+              }
+            }
+            if (mask) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int q_ = it * kKvBq + qb * 32 + 16 * (r >> 3) + 8 * hl + (r & 7);
+                const bool ok = key < n && (!CAUSAL || key <= q_);
+                sv[qb][r] = ok ? sv[qb][r] : s_masked;
+              }
+            }
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+              const float p0 = fast_exp2(__builtin_fmaf(sv[qb][r], c, nl[r]));
+              const float p1 = fast_exp2(__builtin_fmaf(sv[qb][r + 1], c, nl[r + 1]));
+              pb[qb][r >> 3][(r & 7) >> 1] = pack2<IN>(p0, p1);
+            }
+            pbuf[0][kblk][qb][lane] = pb[qb][0];
+            pbuf[1][kblk][qb][lane] = pb[qb][1];
+          }
+        }
+        __syncthreads();  // P is in LDS
+#if FA_BWD_LAG
+        issue(slot_ref(SN{}), it + NS - 1);
+#endif
+        if (lv) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) prod_t(slot.g, qb, pb[qb], acc);  // dV^T += dO^T P
+        }
+      } else {
+        f32x16_t dp[QB];
+#if FA_BWD_LAG
+        // dK^T += Q^T dS of the previous tile, whose slot is refilled only
+        // after the next barrier
+        if (pl) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) prod_t(slot_ref(SN{}).q, qb, dsp[qb], acc);
+        }
+#endif
+        if (lv) prod(slot.g, f, dp);
+        __syncthreads();  // P is in LDS
+#if FA_BWD_LAG
+        issue(slot_ref(SN{}), it + NS - 1);
+#endif
+        if (lv) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const u32x4_t pw[2] = {pbuf[0][kblk][qb][lane], pbuf[1][kblk][qb][lane]};
+            float dd[16];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                const u32x4_t y = *(const u32x4_t*)(slot.st + 256 + qb * 32 + 16 * h + 8 * hl + 4 * e);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dd[8 * h + 4 * e + r] = __uint_as_float(y[r]);
+              }
+            }
+            u32x4_t dsb[2];
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+              float p0, p1;
+              unpack2<IN>(pw[r >> 3][(r & 7) >> 1], p0, p1);
+              dsb[r >> 3][(r & 7) >> 1] = pack2<IN>(p0 * (dp[qb][r] - dd[r]), p1 * (dp[qb][r + 1] - dd[r + 1]));
+            }
+#if FA_BWD_LAG
+            dsp[qb][0] = dsb[0];
+            dsp[qb][1] = dsb[1];
+#else
+            prod_t(slot.q, qb, dsb, acc);  // dK^T += Q^T dS
+#endif
+          }
+        }
+        pl = lv;
+      }
+    };
+
+    for (int i0 = i_lo; i0 < nt; i0 += NS) {
+      step(std::integral_constant<int, 0>{}, i0);
+      if (i0 + 1 < nt) step(std::integral_constant<int, 1>{}, i0 + 1);
+      if constexpr (NS > 2) if (i0 + 2 < nt) step(std::integral_constant<int, 2>{}, i0 + 2);
+      if constexpr (NS > 3) if (i0 + 3 < nt) step(std::integral_constant<int, 3>{}, i0 + 3);
+    }
+#if FA_BWD_LAG
+    if constexpr (!kS) {
+      if (pl) {  // the last tile's dK product (no copy targets its slot any more)
+        const int ls = (nt - 1 - i_lo) % NS;
+        const uint8_t* lq = ls == 0 ? ring0.q : ls == 1 ? ring1.q : ls == 2 ? ring2.q : ring3.q;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) prod_t(lq, qb, dsp[qb], acc);
+      }
+    }
+#endif
+    wait_vmcnt<0>();
+    if (key < n) {
+      if constexpr (kS) store_rows<IN, NDB>((uint16_t*)hv.dv + (size_t)key * (hv.rs / 2), hl, acc, 1.0f);
+      else store_rows<IN, NDB>((uint16_t*)hv.dk + (size_t)key * (hv.rs / 2), hl, acc, a.scale);
+    }
+  };
+  if (w < 4) run(std::true_type{});
+  else run(std::false_type{});
+}
+
 #ifndef FA_BWD_PAIR
 #define FA_BWD_PAIR 1
 #endif
@@ -629,10 +946,12 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   if (a.causal) {
     hipError_t e = launch_kernel(bwd_dq<E, D, true>, dim3(g1), dim3(kDqThreads), s, b);
     if (e != hipSuccess) return e;
+    if (FA_BWD_SPLIT) return launch_kernel(bwd_dkdv2<E, D, true>, dim3(g2), dim3(kKv2Threads), s, a);
     return launch_kernel(bwd_dkdv<E, D, true>, dim3(g2), dim3(kKvThreads), s, a);
   } else {
     hipError_t e = launch_kernel(bwd_dq<E, D, false>, dim3(g1), dim3(kDqThreads), s, b);
     if (e != hipSuccess) return e;
+    if (FA_BWD_SPLIT) return launch_kernel(bwd_dkdv2<E, D, false>, dim3(g2), dim3(kKv2Threads), s, a);
     return launch_kernel(bwd_dkdv<E, D, false>, dim3(g2), dim3(kKvThreads), s, a);
   }
 }
