@@ -802,6 +802,11 @@ def main(argv=None):
                                 KERNEL_OF_DTYPE[w.dtype] + ("+combine_splits" if ws is not None else "")),
                      "min_hbm_bytes": min_hbm_bytes(w)},
     }
+    if traffic is not None:
+        # not counted in this run: the committed FETCH_SIZE / WRITE_SIZE
+        # record, used only while its kernel source hash matches this build
+        line["roofline"]["traffic_source"] = (f"stored counter record {os.path.relpath(TRAFFIC_FILE, ROOT)} "
+                                              f"(kernel source hash {kernel_source_hash()})")
     if not args.no_cold_cache:
         line["cold_cache"] = cold_cache_pass(step, stream, flops)
     if not args.no_cpu_baseline:
