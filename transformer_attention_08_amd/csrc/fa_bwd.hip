@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <climits>
+
 #include <atomic>
 #include <type_traits>
 
@@ -294,12 +296,11 @@ void bwd_dq(BwdArgs a) {
         dp = mfma16<IN>(*(const u32x4_t*)(slot.b + at), gf[ks], dp);
       }
       if (mask) {
+        // register i holds key j*BK + kb*32 + 8*hl + off, off = 16*(i >> 3) +
+        // (i & 7): visible (key < n and, causal, key <= qrow) iff off <= lim
+        const int lim = (CAUSAL ? min(n - 1, qrow) : n - 1) - (j * BK + kb * 32 + 8 * hl);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = j * BK + kb * 32 + 16 * (i >> 3) + 8 * hl + (i & 7);
-          const bool ok = key < n && (!CAUSAL || key <= qrow);
-          s[i] = ok ? s[i] : s_masked;
-        }
+        for (int i = 0; i < 16; ++i) s[i] = 16 * (i >> 3) + (i & 7) <= lim ? s[i] : s_masked;
       }
       u32x4_t dsb[2];
 #pragma unroll
@@ -540,12 +541,11 @@ void bwd_dkdv(BwdArgs a) {
         }
       }
       if (mask) {
+        // register r holds query it*Bq + qb*32 + 8*hl + off, off = 16*(r >> 3)
+        // + (r & 7): visible (key < n and, causal, key <= query) iff off >= lo
+        const int lo = key < n ? (CAUSAL ? key - (it * kKvBq + qb * 32 + 8 * hl) : INT_MIN) : INT_MAX;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int q_ = it * kKvBq + qb * 32 + 16 * (r >> 3) + 8 * hl + (r & 7);
-          const bool ok = key < n && (!CAUSAL || key <= q_);
-          sc[r] = ok ? sc[r] : s_masked;
-        }
+        for (int r = 0; r < 16; ++r) sc[r] = 16 * (r >> 3) + (r & 7) >= lo ? sc[r] : s_masked;
       }
       u32x4_t pb[2], dsb[2];
 #pragma unroll
@@ -827,12 +827,11 @@ void bwd_dkdv2(BwdArgs a) {
               }
             }
             if (mask) {
+              // register r holds query it*Bq + qb*32 + 8*hl + off, off =
+              // 16*(r >> 3) + (r & 7): visible iff off >= lo
+              const int lo = key < n ? (CAUSAL ? key - (it * kKvBq + qb * 32 + 8 * hl) : INT_MIN) : INT_MAX;
 #pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int q_ = it * kKvBq + qb * 32 + 16 * (r >> 3) + 8 * hl + (r & 7);
-                const bool ok = key < n && (!CAUSAL || key <= q_);
-                sv[qb][r] = ok ? sv[qb][r] : s_masked;
-              }
+              for (int r = 0; r < 16; ++r) sv[qb][r] = 16 * (r >> 3) + (r & 7) >= lo ? sv[qb][r] : s_masked;
             }
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {

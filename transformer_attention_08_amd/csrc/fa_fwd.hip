@@ -450,14 +450,17 @@ void fwd_direct(FwdArgs a) {
     f32x16_t s[KB];
     qk_tile<IN, KB, NKS, ROWB>(s, slot.k, krow, kswz, hl, qf);
     if (needs_mask(j)) {
-      const int kbase = j * BK;
+      // register i of key block kb holds key j*BK + 8*hl + off with
+      // off = kb*32 + 16*(i >> 3) + (i & 7), a constant: the key is visible
+      // (key < n and, causal, key <= qrow) iff off <= lim
+      const int kofs = j * BK + 8 * hl;
+      const int lim = (CAUSAL ? min(n - 1, qrow) : n - 1) - kofs;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = kbase + kb * 32 + 16 * (i >> 3) + 8 * hl + (i & 7);
-          const bool ok = key < n && (!CAUSAL || key <= qrow);
-          s[kb][i] = ok ? s[kb][i] : -INFINITY;
+          const int off = kb * 32 + 16 * (i >> 3) + (i & 7);
+          s[kb][i] = off <= lim ? s[kb][i] : -INFINITY;
         }
       }
     }
@@ -720,14 +723,17 @@ void fwd_direct8(FwdArgs a) {
     f32x16_t s[KB];
     qk_tile<Elt::BF16, KB, NKS, ROWB>(s, slot.k, krow, kswz, hl, qf);
     if (needs_mask(j)) {
-      const int kbase = j * BK;
+      // register i of key block kb holds key j*BK + 8*hl + off with
+      // off = kb*32 + 16*(i >> 3) + (i & 7), a constant: the key is visible
+      // (key < n and, causal, key <= qrow) iff off <= lim
+      const int kofs = j * BK + 8 * hl;
+      const int lim = (CAUSAL ? min(n - 1, qrow) : n - 1) - kofs;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = kbase + kb * 32 + 16 * (i >> 3) + 8 * hl + (i & 7);
-          const bool ok = key < n && (!CAUSAL || key <= qrow);
-          s[kb][i] = ok ? s[kb][i] : -INFINITY;
+          const int off = kb * 32 + 16 * (i >> 3) + (i & 7);
+          s[kb][i] = off <= lim ? s[kb][i] : -INFINITY;
         }
       }
     }
