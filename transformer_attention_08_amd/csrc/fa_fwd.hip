@@ -996,6 +996,374 @@ void fwd_mfma32(FwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// fwd_w48: eight waves of 48 query rows (384 per workgroup) on the 16x16x32
+// MFMA, d_k 128, f16 / bf16. Every K operand (16 keys x 32 d-columns) and
+// every V^T operand (16 d-columns x 32 keys) read from LDS feeds the MFMAs
+// of the wave's three 16-row query blocks, and every 64-key tile copied into
+// LDS serves 384 query rows (fwd_direct: one MFMA per operand read, 256
+// rows per tile).
+//
+// 16x16x32 operand layouts: A, lane l: row l % 16, k-elements 8(l/16)..+7;
+// B, lane l: column l % 16, k-elements 8(l/16)..+7; accumulator, lane l:
+// rows 4(l/16)..+3 of column l % 16. Per 16-key sub-tile t of a 64-key tile
+// and query block qb, S^T = K Q^T puts query 16 qb + l % 16 on lane l and
+// keys kt(t, 4(l/16) + i), i < 4, in its registers, with the sub-tile's rows
+// permuted, kt(t, m) = 32 (t >> 1) + 8 (m >> 2) + 4 (t & 1) + (m & 3): the 8
+// keys 32 kb + 8 (l/16) .. + 7 that lane l feeds into one P.V MFMA (B
+// operand, 32 keys) are then its own registers of sub-tiles 2 kb and 2 kb + 1.
+// A query's 64 keys of a tile lie in lanes l, l ^ 16, l ^ 32 and l ^ 48, so
+// the row max takes two lane exchanges.
+// ---------------------------------------------------------------------------
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+#ifndef FA_W48
+#define FA_W48 0
+#endif
+#ifndef FA_W48_STAGES
+#define FA_W48_STAGES 4
+#endif
+#ifndef FA_W48_AHEAD
+#define FA_W48_AHEAD 3
+#endif
+#ifndef FA_W48_PRIO
+#define FA_W48_PRIO 1
+#endif
+constexpr int kW48Waves = 8;
+constexpr int kW48Threads = 64 * kW48Waves;
+constexpr int kW48Rows = 48;
+constexpr int kW48Bq = kW48Rows * kW48Waves;
+#ifndef FA_W48_KEYS
+#define FA_W48_KEYS 32
+#endif
+constexpr int kW48Bk = FA_W48_KEYS;  // keys per tile: 32 or 64
+
+template <Elt E>
+__device__ inline f32x4_t mfma16x16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  if constexpr (E == Elt::F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                   c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Chunk swizzles of the K and V tiles (16-byte chunks of 256-byte rows).
+// K: bijective on the 16 rows of one A-operand read (rows 8m' + (m & 3) + a
+// sub-tile offset), so its 16 lanes per phase hit distinct bank groups. V:
+// even values, distinct over the 8 rows that the 32 lanes of one
+// transposing-read phase address (4 rows each of two lane groups), so the
+// two 16-byte chunks of each row land on distinct bank groups too.
+// max / sum of x over lanes l and l ^ 16 (v_permlane16_swap exchanges the
+// odd and even 16-lane rows of its two operands; with both operands x each
+// lane gets its own value and its partner's)
+__device__ inline float pair16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Largest lane sum of p the 48-row kernel accepts without moving the
+// reference max: each p is then below it, within the 16-bit P operand's
+// range (f16: 65504) and far from fp32 overflow in o and l.
+template <Elt E>
+constexpr float kW48Bound = E == Elt::F16 ? 32768.f : 1.8446744e19f;  // 2^15, 2^64
+
+__device__ inline int w48_kswz(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
+__device__ inline int w48_vswz(int row) { return ((row & 3) | (((row >> 3) & 1) << 2)) << 1; }
+
+template <Elt IN, bool CAUSAL>
+__global__ __launch_bounds__(kW48Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_w48(FwdArgs a) {
+  constexpr int ROWB = 256, BK = kW48Bk, QB = 3, KT = 2, NKS = 4, NDT = 8, NH = BK / 32;
+  static_assert(BK == 32 || BK == 64, "32- or 64-key tiles");
+  constexpr int TILE_B = BK * ROWB;
+  constexpr int LPW = TILE_B / 1024 / kW48Waves;
+  constexpr int NS = FA_W48_STAGES;
+  static_assert(NS >= 3 && NS <= 4, "ring stages");
+  static_assert(LPW >= 1, "tile too small for the wave count");
+
+  __shared__ LdsSlot<TILE_B> ring0, ring1, ring2, ring3;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lm = lane & 15, g = lane >> 4;
+  const int tiles = (a.n + kW48Bq - 1) / kW48Bq;
+  const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL, kW48Bq);
+  const HeadView hv = head_view<2, 2>(a, tl.bh);
+  const int n = hv.n;
+  // n is rarely a multiple of 384: the tiles are laid out from the last row
+  // back, so the partial tile is the first one -- under a causal mask the
+  // one with the fewest keys -- and rows before 0 are masked and not stored.
+  const int tiles_n = (n + kW48Bq - 1) / kW48Bq;
+  if (tl.t >= tiles_n) return;  // a tile past a short sequence (uniform)
+  const int q0 = tl.t * kW48Bq - (tiles_n * kW48Bq - n);
+  const int qw0 = q0 + kW48Rows * w;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(hv.q, span_bytes(n, hv.qrs, ROWB));
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(hv.k, span_bytes(n, hv.krs, ROWB));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(hv.v, span_bytes(n, hv.vrs, ROWB));
+  const KeyTiles kt = key_tiles<BK>(a, n, q0 + kW48Bq, CAUSAL);
+  const int j_lo = kt.lo, nt = kt.hi;
+
+  uint32_t koff[LPW], voff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int byte = (w * LPW + i) * 1024 + lane * 16;
+    const int row = byte / ROWB, p = (byte % ROWB) / 16;
+    koff[i] = (uint32_t)row * hv.krs + (uint32_t)((p ^ w48_kswz(row)) * 16);
+    voff[i] = (uint32_t)row * hv.vrs + (uint32_t)((p ^ w48_vswz(row)) * 16);
+  }
+  auto issue = [&](LdsSlot<TILE_B>& slot, int J) __attribute__((always_inline)) {
+    const uint32_t kb = J < nt ? (uint32_t)(J * BK) * hv.krs : 0x80000000u;
+    const uint32_t vb = J < nt ? (uint32_t)(J * BK) * hv.vrs : 0x80000000u;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      lds_dma16(rk, slot.k + (w * LPW + i) * 1024, kb + koff[i]);
+      lds_dma16(rv, slot.v + (w * LPW + i) * 1024, vb + voff[i]);
+    }
+  };
+
+#if FA_W48_PRIO
+  // waves 0-3 issue ahead of their SIMD partners 4-7, so that one wave's
+  // softmax runs beside the other's MFMAs rather than at the same time
+  if (w < 4) __builtin_amdgcn_s_setprio(FA_W48_PRIO);
+#endif
+  // Q fragments: B operand of S^T = K Q^T, query 16 qb + lm, d-columns
+  // 32 ks + 8 g .. + 7.
+  u32x4_t qf[QB][NKS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int row = qw0 + 16 * qb + lm;  // rows before 0: an offset past the end (zeros)
+      qf[qb][ks] = bload16(rq, row >= 0 ? (uint32_t)row * hv.qrs + (32 * ks + 8 * g) * 2 : 0x80000000u);
+    }
+  }
+  if (a.qneg) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qf[qb][ks] ^= 0x80008000u;
+    }
+  }
+
+  // LDS read offsets. K: sub-tile t's row for lane l is krow + 32 (t >> 1) +
+  // 4 (t & 1) with krow = 8 (lm >> 2) + (lm & 3); its swizzle is lm for
+  // every t. V: the transposing reads of key block kb, half r, d-tile dt
+  // address row 32 kb + 8 g + 4 r + (lm >> 2), bytes 32 dt + 8 (lm & 3) of
+  // the unswizzled row; the row's swizzle is the same for every kb, r.
+  const int krow = 8 * (lm >> 2) + (lm & 3);
+  const int vrow = 8 * g + (lm >> 2);
+  const int vsw = 2 * ((lm >> 2) | ((g & 1) << 2));
+  const int vch = (lm & 3) >> 1, vhalf = (lm & 1) * 8;
+
+  const float c = a.c;
+  float m2[QB], lp[QB];
+  f32x4_t o[NDT][QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m2[qb] = -INFINITY;  // the reference max (base-2 units); see the softmax below
+    lp[qb] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt][qb] = f32x4_t{};
+  }
+  auto live = [&](int j) __attribute__((always_inline)) {
+    return qw0 < n && qw0 + kW48Rows > 0 && !(CAUSAL && j * BK > qw0 + kW48Rows - 1);
+  };
+  auto needs_mask = [&](int j) __attribute__((always_inline)) {
+    return (j * BK + BK > n) || (CAUSAL && j * BK + BK - 1 > qw0);
+  };
+
+  // One tile: NH chunks of 32 keys, each Q K^T (two 16-key sub-tiles), the
+  // softmax and P.V (one 32-key block); the next tile's copies go out after
+  // the first chunk's softmax.
+  auto compute = [&](const LdsSlot<TILE_B>& slot, int j, auto&& mid) __attribute__((always_inline)) {
+    const bool mask = needs_mask(j);
+#pragma unroll 1
+    for (int h = 0; h < NH; ++h) {
+      f32x4_t s[KT][QB];
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[t][qb] = f32x4_t{};
+      }
+      // operand i = (k-step i / KT, sub-tile i % KT), read FA_W48_AHEAD
+      // ahead in a pinned order
+      constexpr int NKO = NKS * KT, KA = FA_W48_AHEAD;
+      auto kread = [&](int i) __attribute__((always_inline)) {
+        const int ks = i / KT, t = i % KT;
+        const int row = 32 * h + krow + 4 * t;
+        return *(const u32x4_t*)(slot.k + row * ROWB + (((4 * ks + g) ^ lm) * 16));
+      };
+      u32x4_t kf[KA];
+#pragma unroll
+      for (int i = 0; i < KA; ++i) kf[i] = kread(i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NKO; ++i) {
+        const int ks = i / KT, t = i % KT;
+        const u32x4_t cur = kf[i % KA];
+        if (i + KA < NKO) kf[i % KA] = kread(i + KA);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[t][qb] = mfma16x16<IN>(cur, qf[qb][ks], s[t][qb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (mask) {
+        // register i of sub-tile t holds key j*BK + 8g + off, off = 32h +
+        // 4t + i: visible iff off <= lim
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int lim = (CAUSAL ? min(n - 1, qw0 + 16 * qb + lm) : n - 1) - (j * BK + 8 * g);
+#pragma unroll
+          for (int t = 0; t < KT; ++t) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int off = 32 * h + 4 * t + i;
+              s[t][qb][i] = off <= lim ? s[t][qb][i] : -INFINITY;
+            }
+          }
+        }
+      }
+      // online softmax without a chunk max on the common path: p against the
+      // row's current reference m. Since p >= 0, a lane's sum of p bounds
+      // each of its p; only when some lane's sum passes kW48Bound (or is not
+      // finite), or a row has no reference yet, does the chunk take the true
+      // max, move the reference, rescale o and l and redo its exponentials.
+      // The result is the same for any reference: m cancels in o / l and the
+      // LSE is m + log2 l for whatever m was used; the first reference is a
+      // true max, so a row's largest weight so far is exactly 1.
+      u32x4_t pb[QB];
+      float ls[QB];
+      auto expo = [&](int qb, float nm) __attribute__((always_inline)) {
+        float acc = 0.f;
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const float p0 = fast_exp2(__builtin_fmaf(s[t][qb][i], c, nm));
+            const float p1 = fast_exp2(__builtin_fmaf(s[t][qb][i + 1], c, nm));
+            acc += p0 + p1;
+            pb[qb][2 * t + (i >> 1)] = pack2<IN>(p0, p1);
+          }
+        }
+        ls[qb] = acc;
+      };
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) expo(qb, -exp_ref(m2[qb]));
+      const float lmax = fmaxf(fmaxf(ls[0], ls[1]), ls[2]);
+      const float mmin = fminf(fminf(m2[0], m2[1]), m2[2]);
+      if (__any(!(lmax <= kW48Bound<IN>) || mmin == -INFINITY)) {
+        float alpha[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          float mx = s[0][qb][0];
+#pragma unroll
+          for (int t = 0; t < KT; ++t) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[t][qb][i]);
+          }
+          mx = pair_max(pair16_max(mx));
+          const float mn = fmaxf(m2[qb], mx * c);  // -inf while the row has seen no visible key
+          alpha[qb] = fast_exp2(m2[qb] - exp_ref(mn));
+          m2[qb] = mn;
+          lp[qb] *= alpha[qb];
+          expo(qb, -exp_ref(mn));
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) o[dt][qb] *= alpha[qb];
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) lp[qb] += ls[qb];
+      if (h == 0) mid();
+      // O^T += V^T P^T: per d-tile one V^T operand (two transposing reads of
+      // four keys each), three MFMAs
+      auto vread = [&](int dt) __attribute__((always_inline)) {
+        const uint8_t* p0 = slot.v + (32 * h + vrow) * ROWB + (((2 * dt + vch) ^ vsw) * 16) + vhalf;
+        const u32x2_t lo = lds_read_tr16(p0);
+        const u32x2_t hi = lds_read_tr16(p0 + 4 * ROWB);
+        return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      };
+      u32x4_t vf[KA];
+#pragma unroll
+      for (int i = 0; i < KA; ++i) vf[i] = vread(i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const u32x4_t cur = vf[dt % KA];
+        if (dt + KA < NDT) vf[dt % KA] = vread(dt + KA);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) o[dt][qb] = mfma16x16<IN>(cur, pb[qb], o[dt][qb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  auto slot_ref = [&](auto S) __attribute__((always_inline)) -> LdsSlot<TILE_B>& {
+    if constexpr (decltype(S)::value == 0) return ring0;
+    else if constexpr (decltype(S)::value == 1) return ring1;
+    else if constexpr (decltype(S)::value == 2) return ring2;
+    else return ring3;
+  };
+  auto step = [&](auto S, int J) __attribute__((always_inline)) {
+    using SN = std::integral_constant<int, (decltype(S)::value + NS - 1) % NS>;
+    wait_vmcnt<(NS - 2) * 2 * LPW>();  // this wave's share of tile J has landed
+    __syncthreads();                   // ... and every other wave's
+    auto refill = [&]() __attribute__((always_inline)) { issue(slot_ref(SN{}), J + NS - 1); };
+    if (live(J)) compute(slot_ref(S), J, refill);
+    else refill();
+  };
+
+  {
+    LdsSlot<TILE_B>* slots[4] = {&ring0, &ring1, &ring2, &ring3};
+#pragma unroll
+    for (int si = 0; si < NS; ++si) {
+      u32x4_t* p = (u32x4_t*)slots[si];
+      for (int i = tid; i < (int)(sizeof(LdsSlot<TILE_B>) / 16); i += kW48Threads) p[i] = u32x4_t{0, 0, 0, 0};
+    }
+  }
+  __syncthreads();
+  issue(ring0, j_lo);
+  issue(ring1, j_lo + 1);
+  if constexpr (NS > 3) issue(ring2, j_lo + 2);
+  // Q and the first tiles have landed: the compiler counts only the Q loads
+  // (the tile copies are inline assembly), and without this full wait it
+  // would wait for the newest loads -- the next tiles' copies -- before
+  // every use of Q inside the loop.
+  wait_vmcnt<0>();
+  for (int J = j_lo; J < nt; J += NS) {
+    step(std::integral_constant<int, 0>{}, J);
+    if (J + 1 < nt) step(std::integral_constant<int, 1>{}, J + 1);
+    if (J + 2 < nt) step(std::integral_constant<int, 2>{}, J + 2);
+    if constexpr (NS > 3) if (J + 3 < nt) step(std::integral_constant<int, 3>{}, J + 3);
+  }
+  wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
+
+  // epilogue: O = o / l per query (the four lanes of a query hold partial l),
+  // LSE = ln 2 (m + log2 l)
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = pair_sum(pair16_sum(lp[qb]));
+    const int row = qw0 + 16 * qb + lm;
+    const float inv = a.o_mult / lt;
+    if (row >= 0 && row < n) {
+      uint16_t* orow = (uint16_t*)hv.o + (size_t)row * hv.ors;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint32_t x0 = pack2<IN>(o[dt][qb][0] * inv, o[dt][qb][1] * inv);
+        const uint32_t x1 = pack2<IN>(o[dt][qb][2] * inv, o[dt][qb][3] * inv);
+        *(u32x2_t*)(orow + 16 * dt + 4 * g) = u32x2_t{x0, x1};
+      }
+      if (g == 0 && hv.lse) hv.lse[row] = (m2[qb] + __log2f(lt)) * kLn2;
+    }
+  }
+}
+
 hipError_t launch(void (*kernel)(FwdArgs), const FwdArgs& a, hipStream_t stream, int rows = kBq,
                   int threads = kThreads) {
   const int tiles = (a.n + rows - 1) / rows;
@@ -1072,6 +1440,18 @@ hipError_t dispatch_causal(const FwdArgs& a, hipStream_t s) {
     return a.causal ? launch(fwd_direct8<D, true>, a, s, kDirectBq, kDirectThreads)
                     : launch(fwd_direct8<D, false>, a, s, kDirectBq, kDirectThreads);
   } else {
+    if constexpr (D == 128 && FA_W48 != 0) {
+      const int wt = (a.n + kW48Bq - 1) / kW48Bq;
+      // 384-row tiles only where they still give every CU two or more
+      // workgroups (shorter heads keep the 256-row kernel's balance); ragged
+      // batches stay on the 256-row kernel, so that each sequence's result
+      // is the one a dense call on it returns
+      if (!a.cu_seqlens && a.splits == 1 && !a.part_o && (long)a.bh * wt >= 2L * device_cus()) {
+        const dim3 grid((unsigned)a.bh * (unsigned)wt, 1u);
+        return a.causal ? launch_kernel(fwd_w48<E, true>, grid, dim3(kW48Threads), s, a)
+                        : launch_kernel(fwd_w48<E, false>, grid, dim3(kW48Threads), s, a);
+      }
+    }
     const int tiles = (a.n + kDirectBq - 1) / kDirectBq;
     // Pairs of equal tiles (no mask) only when the paired grid still fills
     // every CU; causal pairs are never longer than the longest unpaired tile.
