@@ -48,6 +48,20 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "fp8": 5033.2, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 # the kernel each input type runs on
 KERNEL_OF_DTYPE = {"bf16": "fwd_direct", "f16": "fwd_direct", "fp8": "fwd_direct8", "f32": "fwd_mfma32"}
+# f16 / bf16 heads of d_k 128 and at least this many rows run on the 384-row
+# kernel fwd_w48 (unsplit, dense batches, two or more of its workgroups per CU);
+# the same rule as the forward dispatch in fa_fwd.hip
+W48_MIN_N, W48_ROWS = 16384, 384
+
+
+def fwd_kernel(w, split: bool, ragged: bool = False) -> str:
+    """Name of the forward kernel fa_forward launches for workload w."""
+    if w.dtype in ("bf16", "f16") and w.d_k == 128 and w.n >= W48_MIN_N and not split and not ragged:
+        import torch
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        if w.batch * w.heads * -(-w.n // W48_ROWS) >= 2 * cus:
+            return "fwd_w48"
+    return KERNEL_OF_DTYPE[w.dtype]
 # the files the forward kernels and their launch shape are compiled from; a
 # stored traffic measurement is valid only for the sources it was taken on
 KERNEL_SOURCES = ("transformer_attention_08_amd/csrc/fa_fwd.hip",
@@ -569,7 +583,7 @@ def bench_backward(args, w):
         "ms_min": round(min(per), 5),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": None,
-                     "kernel": "bwd_dq+bwd_dkdv"},
+                     "kernel": "bwd_dq+bwd_dkdv2"},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_backward(w, inp, do)
@@ -632,7 +646,7 @@ def bench_varlen(args, w):
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "ms_median": round(statistics.median(per), 5),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": None, "kernel": KERNEL_OF_DTYPE[w.dtype]},
+                     "frac": round(tflops / peak, 4), "traffic": None, "kernel": fwd_kernel(w, False, True)},
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -799,7 +813,7 @@ def main(argv=None):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": traffic,
                      "kernel": ("unf_scores+unf_softmax+unf_pv" if uws is not None else
-                                KERNEL_OF_DTYPE[w.dtype] + ("+combine_splits" if ws is not None else "")),
+                                fwd_kernel(w, ws is not None) + ("+combine_splits" if ws is not None else "")),
                      "min_hbm_bytes": min_hbm_bytes(w)},
     }
     if traffic is not None:

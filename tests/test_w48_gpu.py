@@ -1,0 +1,133 @@
+"""GPU parity of the 384-row forward kernel (fwd_w48) against the fp64 oracle.
+
+fa_forward runs f16 / bf16 heads of d_k 128 with n >= 16384 rows on the
+48-row-per-wave kernel when its grid gives every compute unit two or more
+workgroups (12 heads of n <= 18432 on a 256-CU device). Its tiles are laid
+out from the last row back, so a ragged n leaves a partial first tile whose
+missing rows lie before row 0, and its softmax takes no chunk max unless a
+lane's sum of p passes 2^64 (bf16) or 2^15 (f16). The shapes below take both
+paths; rows are a seeded sample (the first and last rows of every head plus
+random ones), computed by the oracle row by row.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workload
+from parity_util import O_TOL, LSE_TOL, gpu_forward, oracle_forward, report
+
+pytestmark = pytest.mark.gpu
+
+OUT_FMT = {"f16": "f16", "bf16": "bf16"}
+D = 128
+SCALE = float(np.float32(1 / math.sqrt(D)))
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def check_rows(inp, causal, rows):
+    o, lse = gpu_forward(inp, causal, SCALE)
+    o, lse = o[:, :, rows], lse[:, :, rows]
+    o_ref, lse_ref = oracle_forward(inp, causal, SCALE, rows=rows)
+    r = report(o, lse, o_ref, lse_ref, OUT_FMT[inp.dtype])
+    say("   ", r)
+    assert r["finite"]
+    assert r["lse_max"] <= LSE_TOL, r
+    assert r["o_max"] <= O_TOL[inp.dtype], r
+
+
+def _dev(t):
+    return t.to("cuda")
+
+
+@pytest.mark.parametrize("dtype,causal,heads,n", [
+    ("bf16", True, 12, 16384),    # the smallest n that takes the kernel; 43 tiles, the first 256 rows
+    ("bf16", False, 12, 16500),   # first tile holds 372 rows
+    ("f16", True, 12, 17000),     # first tile holds 104 rows
+    ("f16", False, 10, 20000),    # 53 tiles x 10 heads
+])
+def test_w48_sampled_rows(dtype, causal, heads, n):
+    say(f"w48 [1, {heads}, {n}, {D}] {dtype} causal={causal}")
+    inp = workload.make_inputs(1, heads, n, D, dtype, seed=n + heads)
+    rows = workload.sample_rows(n, 768, seed=n)
+    check_rows(inp, causal, rows)
+
+
+def growing_scores(heads, n, dtype, seed, rise=120.0):
+    """Q and K whose scores rise along the keys by about `rise` (natural-log
+    units) from key 0 to key n - 1, with N(0, 1) noise on every element: each
+    later 32-key chunk outscores the reference the first chunk set, so lane
+    sums of p pass the bound several times per row (every ~44 units in bf16,
+    ~10 in f16) and the chunk takes its true max."""
+    g = torch.Generator().manual_seed(seed)
+    u = torch.randn(D, generator=g, dtype=torch.float64)
+    u = u / u.norm()
+    c = 8.0
+    t = torch.arange(n, dtype=torch.float64) * (rise / (SCALE * c) / n)
+    q = c * u + torch.randn(1, heads, n, D, generator=g, dtype=torch.float64)
+    k = t[:, None] * u + torch.randn(1, heads, n, D, generator=g, dtype=torch.float64)
+    v = torch.randn(1, heads, n, D, generator=g, dtype=torch.float64)
+    td = workload.torch_dtype(dtype)
+    return workload.Inputs(q.to(td), k.to(td), v.to(td), dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_w48_growing_scores(dtype, causal):
+    n, heads = 16500, 12
+    say(f"w48 growing scores [1, {heads}, {n}, {D}] {dtype} causal={causal}")
+    inp = growing_scores(heads, n, dtype, seed=21)
+    rows = workload.sample_rows(n, 512, seed=21)
+    check_rows(inp, causal, rows)
+
+
+def test_w48_strided_is_bitwise_dense():
+    """[batch, n, heads, d_k] inputs and output give bitwise the dense result."""
+    import transformer_attention_08_amd as fa
+    n, heads = 16500, 12
+    say(f"w48 strided [1, {n}, {heads}, {D}] bf16 causal")
+    inp = workload.make_inputs(1, heads, n, D, "bf16", seed=31)
+    q, k, v = _dev(inp.q), _dev(inp.k), _dev(inp.v)
+    o1, l1 = fa.forward(q, k, v, causal=True)
+    qs, ks, vs = (t.transpose(1, 2).contiguous() for t in (q, k, v))
+    o2, l2 = fa.forward_strided(qs, ks, vs, layout="bshd", causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2.transpose(1, 2)) and torch.equal(l1, l2)
+
+
+def test_w48_deterministic_and_lse_null():
+    import transformer_attention_08_amd as fa
+    n, heads = 17000, 12
+    say(f"w48 determinism, lse null [1, {heads}, {n}, {D}] f16 causal")
+    inp = workload.make_inputs(1, heads, n, D, "f16", seed=32)
+    q, k, v = _dev(inp.q), _dev(inp.k), _dev(inp.v)
+    o1, l1 = fa.forward(q, k, v, causal=True)
+    o2, l2 = fa.forward(q, k, v, causal=True)
+    o3, l3 = fa.forward(q, k, v, causal=True, want_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert l3 is None and torch.equal(o1, o3)
+
+
+def test_w48_writes_only_rows_of_the_heads():
+    """The partial first tile's missing rows (before row 0) and the rows past
+    n are never written: sentinels on both sides of O and LSE survive."""
+    import transformer_attention_08_amd as fa
+    n, heads = 16500, 12
+    say(f"w48 no write outside [1, {heads}, {n}, {D}] bf16 causal")
+    inp = workload.make_inputs(1, heads, n, D, "bf16", seed=33)
+    pad = 384 * D
+    size = heads * n * D
+    big = torch.full((pad + size + pad,), 7.0, dtype=torch.bfloat16, device="cuda")
+    o = big[pad: pad + size].view(1, heads, n, D)
+    lbig = torch.full((384 + heads * n + 384,), 7.0, dtype=torch.float32, device="cuda")
+    lse = lbig[384: 384 + heads * n].view(1, heads, n)
+    fa.forward(_dev(inp.q), _dev(inp.k), _dev(inp.v), causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert (big[:pad] == 7.0).all() and (big[pad + size:] == 7.0).all()
+    assert (lbig[:384] == 7.0).all() and (lbig[384 + heads * n:] == 7.0).all()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()

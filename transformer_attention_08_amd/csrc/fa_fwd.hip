@@ -998,33 +998,40 @@ void fwd_mfma32(FwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // fwd_w48: eight waves of 48 query rows (384 per workgroup) on the 16x16x32
-// MFMA, d_k 128, f16 / bf16. Every K operand (16 keys x 32 d-columns) and
-// every V^T operand (16 d-columns x 32 keys) read from LDS feeds the MFMAs
-// of the wave's three 16-row query blocks, and every 64-key tile copied into
-// LDS serves 384 query rows (fwd_direct: one MFMA per operand read, 256
-// rows per tile).
+// MFMA, d_k 128, f16 / bf16; the kernel for long heads. Every K operand (16
+// keys x 32 d-columns) and every V^T operand (16 d-columns x 32 keys) read
+// from LDS feeds the MFMAs of the wave's three 16-row query blocks, and every
+// key tile copied into LDS serves 384 query rows (fwd_direct: one MFMA per
+// operand read, 256 rows per tile), so both the LDS operand reads and the
+// L2 -> LDS copies per FLOP are a third lower. 32-key tiles in a 6-slot ring
+// (96 KiB), one workgroup barrier per two tiles.
 //
 // 16x16x32 operand layouts: A, lane l: row l % 16, k-elements 8(l/16)..+7;
 // B, lane l: column l % 16, k-elements 8(l/16)..+7; accumulator, lane l:
-// rows 4(l/16)..+3 of column l % 16. Per 16-key sub-tile t of a 64-key tile
+// rows 4(l/16)..+3 of column l % 16. Per 16-key sub-tile t of a 32-key chunk
 // and query block qb, S^T = K Q^T puts query 16 qb + l % 16 on lane l and
 // keys kt(t, 4(l/16) + i), i < 4, in its registers, with the sub-tile's rows
-// permuted, kt(t, m) = 32 (t >> 1) + 8 (m >> 2) + 4 (t & 1) + (m & 3): the 8
-// keys 32 kb + 8 (l/16) .. + 7 that lane l feeds into one P.V MFMA (B
-// operand, 32 keys) are then its own registers of sub-tiles 2 kb and 2 kb + 1.
-// A query's 64 keys of a tile lie in lanes l, l ^ 16, l ^ 32 and l ^ 48, so
-// the row max takes two lane exchanges.
+// permuted, kt(t, m) = 8 (m >> 2) + 4 t + (m & 3): the 8 keys 8 (l/16) .. + 7
+// that lane l feeds into the chunk's P.V MFMA (B operand, 32 keys) are then
+// its own registers of sub-tiles 0 and 1. A query's 32 keys lie in lanes l,
+// l ^ 16, l ^ 32 and l ^ 48.
 // ---------------------------------------------------------------------------
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 #ifndef FA_W48
-#define FA_W48 0
+#define FA_W48 1
 #endif
 #ifndef FA_W48_STAGES
-#define FA_W48_STAGES 4
+#define FA_W48_STAGES 6
 #endif
 #ifndef FA_W48_AHEAD
 #define FA_W48_AHEAD 3
+#endif
+#ifndef FA_W48_MIN_N
+#define FA_W48_MIN_N 16384
+#endif
+#ifndef FA_W48_GROUP
+#define FA_W48_GROUP 2  // key tiles per workgroup barrier (1, 2 or 3; the ring has 3x as many slots)
 #endif
 #ifndef FA_W48_PRIO
 #define FA_W48_PRIO 1
@@ -1072,6 +1079,16 @@ __device__ inline float pair16_sum(float x) {
 template <Elt E>
 constexpr float kW48Bound = E == Elt::F16 ? 32768.f : 1.8446744e19f;  // 2^15, 2^64
 
+template <int NSL, int BYTES>
+struct W48Ring {
+  __attribute__((aligned(1024))) uint8_t k[NSL][BYTES];
+  __attribute__((aligned(1024))) uint8_t v[NSL][BYTES];
+};
+struct SlotView {
+  uint8_t* k;
+  uint8_t* v;
+};
+
 __device__ inline int w48_kswz(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
 __device__ inline int w48_vswz(int row) { return ((row & 3) | (((row >> 3) & 1) << 2)) << 1; }
 
@@ -1083,10 +1100,13 @@ void fwd_w48(FwdArgs a) {
   constexpr int TILE_B = BK * ROWB;
   constexpr int LPW = TILE_B / 1024 / kW48Waves;
   constexpr int NS = FA_W48_STAGES;
-  static_assert(NS >= 3 && NS <= 4, "ring stages");
+  static_assert(FA_W48_GROUP > 1 ? NS == 3 * FA_W48_GROUP : (NS >= 3 && NS <= 4), "ring stages");
+  static_assert(FA_W48_GROUP >= 1 && FA_W48_GROUP <= 3, "tiles per barrier");
   static_assert(LPW >= 1, "tile too small for the wave count");
 
-  __shared__ LdsSlot<TILE_B> ring0, ring1, ring2, ring3;
+  // K tiles and V tiles in two arrays, so that every slot's reads are one
+  // lane register plus an immediate offset below 64 KiB
+  __shared__ W48Ring<NS, TILE_B> ring;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1116,7 +1136,7 @@ void fwd_w48(FwdArgs a) {
     koff[i] = (uint32_t)row * hv.krs + (uint32_t)((p ^ w48_kswz(row)) * 16);
     voff[i] = (uint32_t)row * hv.vrs + (uint32_t)((p ^ w48_vswz(row)) * 16);
   }
-  auto issue = [&](LdsSlot<TILE_B>& slot, int J) __attribute__((always_inline)) {
+  auto issue = [&](SlotView slot, int J) __attribute__((always_inline)) {
     const uint32_t kb = J < nt ? (uint32_t)(J * BK) * hv.krs : 0x80000000u;
     const uint32_t vb = J < nt ? (uint32_t)(J * BK) * hv.vrs : 0x80000000u;
 #pragma unroll
@@ -1180,7 +1200,7 @@ void fwd_w48(FwdArgs a) {
   // One tile: NH chunks of 32 keys, each Q K^T (two 16-key sub-tiles), the
   // softmax and P.V (one 32-key block); the next tile's copies go out after
   // the first chunk's softmax.
-  auto compute = [&](const LdsSlot<TILE_B>& slot, int j, auto&& mid) __attribute__((always_inline)) {
+  auto compute = [&](const SlotView slot, int j, auto&& mid) __attribute__((always_inline)) {
     const bool mask = needs_mask(j);
 #pragma unroll 1
     for (int h = 0; h < NH; ++h) {
@@ -1304,12 +1324,33 @@ void fwd_w48(FwdArgs a) {
     }
   };
 
-  auto slot_ref = [&](auto S) __attribute__((always_inline)) -> LdsSlot<TILE_B>& {
-    if constexpr (decltype(S)::value == 0) return ring0;
-    else if constexpr (decltype(S)::value == 1) return ring1;
-    else if constexpr (decltype(S)::value == 2) return ring2;
-    else return ring3;
+  auto slot_ref = [&](auto S) __attribute__((always_inline)) -> SlotView {
+    return SlotView{ring.k[decltype(S)::value], ring.v[decltype(S)::value]};
   };
+#if FA_W48_GROUP > 1
+  // One barrier per group of GB tiles (NS = 3 GB slots): at a group's first
+  // step every wave is past the previous group, whose slots take the group
+  // after next; the other steps neither wait nor copy.
+  constexpr int GB = FA_W48_GROUP;
+  auto step = [&](auto S, int J) __attribute__((always_inline)) {
+    constexpr int sv = decltype(S)::value;
+    if constexpr (sv % GB == 0) {
+      wait_vmcnt<GB * 2 * LPW>();  // this group's tiles have landed (the next group's may not)
+      __syncthreads();
+      auto refill = [&]() __attribute__((always_inline)) {
+        issue(slot_ref(std::integral_constant<int, (sv + 2 * GB) % NS>{}), J + 2 * GB);
+        issue(slot_ref(std::integral_constant<int, (sv + 2 * GB + 1) % NS>{}), J + 2 * GB + 1);
+        if constexpr (GB > 2) issue(slot_ref(std::integral_constant<int, (sv + 2 * GB + 2) % NS>{}), J + 2 * GB + 2);
+      };
+      if (live(J)) compute(slot_ref(S), J, refill);
+      else refill();
+    } else {
+      __builtin_amdgcn_sched_barrier(0);  // no motion across the step boundary
+      if (live(J)) compute(slot_ref(S), J, []() {});
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+#else
   auto step = [&](auto S, int J) __attribute__((always_inline)) {
     using SN = std::integral_constant<int, (decltype(S)::value + NS - 1) % NS>;
     wait_vmcnt<(NS - 2) * 2 * LPW>();  // this wave's share of tile J has landed
@@ -1318,19 +1359,21 @@ void fwd_w48(FwdArgs a) {
     if (live(J)) compute(slot_ref(S), J, refill);
     else refill();
   };
+#endif
 
   {
-    LdsSlot<TILE_B>* slots[4] = {&ring0, &ring1, &ring2, &ring3};
-#pragma unroll
-    for (int si = 0; si < NS; ++si) {
-      u32x4_t* p = (u32x4_t*)slots[si];
-      for (int i = tid; i < (int)(sizeof(LdsSlot<TILE_B>) / 16); i += kW48Threads) p[i] = u32x4_t{0, 0, 0, 0};
-    }
+    u32x4_t* p = (u32x4_t*)&ring;
+    for (int i = tid; i < (int)(sizeof(ring) / 16); i += kW48Threads) p[i] = u32x4_t{0, 0, 0, 0};
   }
   __syncthreads();
-  issue(ring0, j_lo);
-  issue(ring1, j_lo + 1);
-  if constexpr (NS > 3) issue(ring2, j_lo + 2);
+  issue(slot_ref(std::integral_constant<int, 0>{}), j_lo);
+  issue(slot_ref(std::integral_constant<int, 1>{}), j_lo + 1);
+  if constexpr (NS > 3) issue(slot_ref(std::integral_constant<int, 2>{}), j_lo + 2);
+  if constexpr (FA_W48_GROUP > 1) issue(slot_ref(std::integral_constant<int, 3>{}), j_lo + 3);
+  if constexpr (FA_W48_GROUP > 2) {
+    issue(slot_ref(std::integral_constant<int, 4>{}), j_lo + 4);
+    issue(slot_ref(std::integral_constant<int, 5>{}), j_lo + 5);
+  }
   // Q and the first tiles have landed: the compiler counts only the Q loads
   // (the tile copies are inline assembly), and without this full wait it
   // would wait for the newest loads -- the next tiles' copies -- before
@@ -1341,6 +1384,11 @@ void fwd_w48(FwdArgs a) {
     if (J + 1 < nt) step(std::integral_constant<int, 1>{}, J + 1);
     if (J + 2 < nt) step(std::integral_constant<int, 2>{}, J + 2);
     if constexpr (NS > 3) if (J + 3 < nt) step(std::integral_constant<int, 3>{}, J + 3);
+    if constexpr (NS > 4) if (J + 4 < nt) step(std::integral_constant<int, 4>{}, J + 4);
+    if constexpr (NS > 5) if (J + 5 < nt) step(std::integral_constant<int, 5>{}, J + 5);
+    if constexpr (NS > 6) if (J + 6 < nt) step(std::integral_constant<int, 6>{}, J + 6);
+    if constexpr (NS > 7) if (J + 7 < nt) step(std::integral_constant<int, 7>{}, J + 7);
+    if constexpr (NS > 8) if (J + 8 < nt) step(std::integral_constant<int, 8>{}, J + 8);
   }
   wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
 
@@ -1442,11 +1490,12 @@ hipError_t dispatch_causal(const FwdArgs& a, hipStream_t s) {
   } else {
     if constexpr (D == 128 && FA_W48 != 0) {
       const int wt = (a.n + kW48Bq - 1) / kW48Bq;
-      // 384-row tiles only where they still give every CU two or more
-      // workgroups (shorter heads keep the 256-row kernel's balance); ragged
-      // batches stay on the 256-row kernel, so that each sequence's result
-      // is the one a dense call on it returns
-      if (!a.cu_seqlens && a.splits == 1 && !a.part_o && (long)a.bh * wt >= 2L * device_cus()) {
+      // 384-row tiles for long heads (n >= FA_W48_MIN_N), where they measured
+      // faster, and only while they give every CU two or more workgroups;
+      // ragged batches, split keys and partial outputs stay on the 256-row
+      // kernel
+      if (!a.cu_seqlens && a.splits == 1 && !a.part_o && a.n >= FA_W48_MIN_N &&
+          (long)a.bh * wt >= 2L * device_cus()) {
         const dim3 grid((unsigned)a.bh * (unsigned)wt, 1u);
         return a.causal ? launch_kernel(fwd_w48<E, true>, grid, dim3(kW48Threads), s, a)
                         : launch_kernel(fwd_w48<E, false>, grid, dim3(kW48Threads), s, a);
