@@ -34,6 +34,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import statistics
 import sys
 import time
@@ -48,19 +49,26 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "fp8": 5033.2, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 # the kernel each input type runs on
 KERNEL_OF_DTYPE = {"bf16": "fwd_direct", "f16": "fwd_direct", "fp8": "fwd_direct8", "f32": "fwd_mfma32"}
-# f16 / bf16 heads of d_k 128 and at least this many rows run on the 384-row
-# kernel fwd_w48 (unsplit, dense batches, two or more of its workgroups per CU);
-# the same rule as the forward dispatch in fa_fwd.hip
-W48_MIN_N, W48_ROWS = 16384, 384
+# f16 / bf16 heads of d_k 128 run on the 384-row kernels (unsplit, dense
+# batches, two or more 384-row tiles per CU): causal heads of W48_PACK_MIN_N
+# <= n < W48_MIN_N on fwd_w48_packed (while every head gets two or more
+# workgroups), heads of n >= W48_MIN_N on fwd_w48; the same rule as the
+# forward dispatch in fa_fwd.hip
+W48_PACK_MIN_N, W48_MIN_N, W48_ROWS = 8192, 16384, 384
 
 
 def fwd_kernel(w, split: bool, ragged: bool = False) -> str:
     """Name of the forward kernel fa_forward launches for workload w."""
-    if w.dtype in ("bf16", "f16") and w.d_k == 128 and w.n >= W48_MIN_N and not split and not ragged:
+    if w.dtype in ("bf16", "f16") and w.d_k == 128 and not split and not ragged:
         import torch
         cus = torch.cuda.get_device_properties(0).multi_processor_count
-        if w.batch * w.heads * -(-w.n // W48_ROWS) >= 2 * cus:
-            return "fwd_w48"
+        bh, tiles = w.batch * w.heads, -(-w.n // W48_ROWS)
+        if bh * tiles >= 2 * cus:
+            if (w.causal and W48_PACK_MIN_N <= w.n < W48_MIN_N and tiles <= 255
+                    and 2 <= cus // bh <= 255):
+                return "fwd_w48_packed"
+            if w.n >= W48_MIN_N:
+                return "fwd_w48"
     return KERNEL_OF_DTYPE[w.dtype]
 # the files the forward kernels and their launch shape are compiled from; a
 # stored traffic measurement is valid only for the sources it was taken on
@@ -186,7 +194,12 @@ def traffic_record(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out=TRA
             raise RuntimeError(f"no {kern} dispatch in {path}")
         return v
 
-    fv, wv = vals(fetch_csv, "fwd_direct"), vals(write_csv, "fwd_direct")
+    # the forward kernel the counted run launched (one name across the file)
+    names = {r["Kernel_Name"] for r in csv.DictReader(open(fetch_csv)) if "::fwd_" in r["Kernel_Name"]}
+    if len(names) != 1:
+        raise RuntimeError(f"expected one forward kernel in {fetch_csv}, found {sorted(names)}")
+    kname = re.search(r"::(fwd_\w+)<", names.pop()).group(1)
+    fv, wv = vals(fetch_csv, f"::{kname}<"), vals(write_csv, f"::{kname}<")
     cfv, cwv = vals(copy_fetch_csv, "copyBuffer"), vals(copy_write_csv, "copyBuffer")
     fetch, write = sum(fv) / len(fv), sum(wv) / len(wv)
     cfk, cwk = sum(cfv) / len(cfv), sum(cwv) / len(cwv)
@@ -197,7 +210,7 @@ def traffic_record(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out=TRA
     mn = min_hbm_bytes(workload.WORKLOADS["llama3_8b_bf16_causal"])
     bench_cmd = "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-cold-cache"
     t = {
-        "kernel": "fwd_direct<bf16, d_k 128, causal>",
+        "kernel": f"{kname}<bf16, d_k 128, causal>",
         "workload": "llama3_8b_bf16_causal [1, 32, 8192, 128]",
         "kernel_source_hash": kernel_source_hash(),
         "kernel_sources": list(KERNEL_SOURCES),

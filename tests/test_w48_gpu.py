@@ -1,13 +1,17 @@
-"""GPU parity of the 384-row forward kernel (fwd_w48) against the fp64 oracle.
+"""GPU parity of the 384-row forward kernels (fwd_w48, fwd_w48_packed)
+against the fp64 oracle.
 
-fa_forward runs f16 / bf16 heads of d_k 128 with n >= 16384 rows on the
-48-row-per-wave kernel when its grid gives every compute unit two or more
-workgroups (12 heads of n <= 18432 on a 256-CU device). Its tiles are laid
-out from the last row back, so a ragged n leaves a partial first tile whose
-missing rows lie before row 0, and its softmax takes no chunk max unless a
-lane's sum of p passes 2^64 (bf16) or 2^15 (f16). The shapes below take both
-paths; rows are a seeded sample (the first and last rows of every head plus
-random ones), computed by the oracle row by row.
+fa_forward runs f16 / bf16 heads of d_k 128 on 48-row-per-wave kernels when
+there are two or more 384-row tiles per compute unit (heads x tiles >= 512
+on a 256-CU device): causal heads of 8192 <= n < 16384 with the tiles packed into groups of near-equal length
+(one workgroup per group; with a multiple of 8 heads, each workgroup may
+take two or more heads in turn), heads of n >= 16384 with one workgroup per
+tile. Tiles are laid out from the last row back, so a ragged n leaves a
+partial first tile whose missing rows lie before row 0, and the softmax
+takes no chunk max unless a lane's sum of p passes 2^64 (bf16) or 2^15
+(f16). The shapes below take each path; rows are a seeded sample (the first
+and last rows of every head plus random ones), computed by the oracle row by
+row.
 """
 import math
 
@@ -45,10 +49,14 @@ def _dev(t):
 
 
 @pytest.mark.parametrize("dtype,causal,heads,n", [
-    ("bf16", True, 12, 16384),    # the smallest n that takes the kernel; 43 tiles, the first 256 rows
-    ("bf16", False, 12, 16500),   # first tile holds 372 rows
-    ("f16", True, 12, 17000),     # first tile holds 104 rows
-    ("f16", False, 10, 20000),    # 53 tiles x 10 heads
+    ("bf16", True, 12, 16384),    # one workgroup per tile; 43 tiles, the first holds 256 rows
+    ("bf16", False, 12, 16500),   # one workgroup per tile; first tile holds 372 rows
+    ("f16", True, 12, 17000),     # one workgroup per tile; first tile holds 104 rows
+    ("f16", False, 10, 20000),    # one workgroup per tile, 53 tiles x 10 heads
+    ("bf16", True, 32, 16384),    # one workgroup per tile, heads one at a time per XCD
+    ("f16", True, 12, 16200),     # packed, 21 groups per head (12 heads: no XCD grouping); first tile 72 rows
+    ("f16", True, 32, 8192),      # packed, 8 groups per head, one head per workgroup
+    ("bf16", True, 64, 8200),     # packed, 8 groups per head, two heads in turn; first tile 136 rows
 ])
 def test_w48_sampled_rows(dtype, causal, heads, n):
     say(f"w48 [1, {heads}, {n}, {D}] {dtype} causal={causal}")
@@ -76,9 +84,9 @@ def growing_scores(heads, n, dtype, seed, rise=120.0):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("causal", [True, False])
-def test_w48_growing_scores(dtype, causal):
-    n, heads = 16500, 12
+@pytest.mark.parametrize("causal,n", [(True, 16500), (False, 16500), (True, 16200)])
+def test_w48_growing_scores(dtype, causal, n):
+    heads = 12
     say(f"w48 growing scores [1, {heads}, {n}, {D}] {dtype} causal={causal}")
     inp = growing_scores(heads, n, dtype, seed=21)
     rows = workload.sample_rows(n, 512, seed=21)
@@ -99,9 +107,10 @@ def test_w48_strided_is_bitwise_dense():
     assert torch.equal(o1, o2.transpose(1, 2)) and torch.equal(l1, l2)
 
 
-def test_w48_deterministic_and_lse_null():
+@pytest.mark.parametrize("n", [17000, 16200])
+def test_w48_deterministic_and_lse_null(n):
     import transformer_attention_08_amd as fa
-    n, heads = 17000, 12
+    heads = 12
     say(f"w48 determinism, lse null [1, {heads}, {n}, {D}] f16 causal")
     inp = workload.make_inputs(1, heads, n, D, "f16", seed=32)
     q, k, v = _dev(inp.q), _dev(inp.k), _dev(inp.v)
@@ -113,11 +122,12 @@ def test_w48_deterministic_and_lse_null():
     assert l3 is None and torch.equal(o1, o3)
 
 
-def test_w48_writes_only_rows_of_the_heads():
+@pytest.mark.parametrize("n", [16500, 16200])
+def test_w48_writes_only_rows_of_the_heads(n):
     """The partial first tile's missing rows (before row 0) and the rows past
     n are never written: sentinels on both sides of O and LSE survive."""
     import transformer_attention_08_amd as fa
-    n, heads = 16500, 12
+    heads = 12
     say(f"w48 no write outside [1, {heads}, {n}, {D}] bf16 causal")
     inp = workload.make_inputs(1, heads, n, D, "bf16", seed=33)
     pad = 384 * D

@@ -43,6 +43,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -1025,7 +1026,13 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 #define FA_W48_STAGES 6
 #endif
 #ifndef FA_W48_AHEAD
-#define FA_W48_AHEAD 3
+#define FA_W48_AHEAD 3  // K operands read ahead, one workgroup per tile
+#endif
+#ifndef FA_W48_PACK_AHEAD
+#define FA_W48_PACK_AHEAD 4  // the same, packed causal tiles
+#endif
+#ifndef FA_W48_PACK_MIN_N
+#define FA_W48_PACK_MIN_N 8192
 #endif
 #ifndef FA_W48_MIN_N
 #define FA_W48_MIN_N 16384
@@ -1044,6 +1051,20 @@ constexpr int kW48Bq = kW48Rows * kW48Waves;
 #define FA_W48_KEYS 32
 #endif
 constexpr int kW48Bk = FA_W48_KEYS;  // keys per tile: 32 or 64
+#ifndef FA_W48_PACK
+#define FA_W48_PACK 1
+#endif
+// Query tiles per head that a packed causal launch can take (n <= 97920).
+constexpr int kW48PlanTiles = 255;
+struct W48Plan {
+  int bins;                            // groups of tiles per head
+  int heads_seq;                       // heads each workgroup takes one after another
+  uint8_t bin_of_tile[kW48PlanTiles];  // the group (0 .. bins-1) of each query tile
+};
+struct W48Args {
+  FwdArgs a;
+  W48Plan plan;
+};
 
 template <Elt E>
 __device__ inline f32x4_t mfma16x16(u32x4_t a, u32x4_t b, f32x4_t c) {
@@ -1092,9 +1113,15 @@ struct SlotView {
 __device__ inline int w48_kswz(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
 __device__ inline int w48_vswz(int row) { return ((row & 3) | (((row >> 3) & 1) << 2)) << 1; }
 
-template <Elt IN, bool CAUSAL>
-__global__ __launch_bounds__(kW48Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fwd_w48(FwdArgs a) {
+// K tiles and V tiles in two arrays, so that every slot's reads are one lane
+// register plus an immediate offset below 64 KiB
+using W48RingT = W48Ring<FA_W48_STAGES, kW48Bk * 256>;
+
+// One 384-row query tile (head tl.bh, tile tl.t), from its Q loads to its
+// O and LSE stores, with the workgroup's LDS ring.
+template <Elt IN, bool CAUSAL, int KA>
+__device__ __attribute__((always_inline)) inline void w48_tile(const FwdArgs& a, W48RingT& ring,
+                                                               const TileId tl) {
   constexpr int ROWB = 256, BK = kW48Bk, QB = 3, KT = 2, NKS = 4, NDT = 8, NH = BK / 32;
   static_assert(BK == 32 || BK == 64, "32- or 64-key tiles");
   constexpr int TILE_B = BK * ROWB;
@@ -1104,15 +1131,13 @@ void fwd_w48(FwdArgs a) {
   static_assert(FA_W48_GROUP >= 1 && FA_W48_GROUP <= 3, "tiles per barrier");
   static_assert(LPW >= 1, "tile too small for the wave count");
 
-  // K tiles and V tiles in two arrays, so that every slot's reads are one
-  // lane register plus an immediate offset below 64 KiB
-  __shared__ W48Ring<NS, TILE_B> ring;
-
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, lm = lane & 15, g = lane >> 4;
-  const int tiles = (a.n + kW48Bq - 1) / kW48Bq;
-  const TileId tl = tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL, kW48Bq);
+  // The lane index comes from the execution mask (mbcnt) and passes through
+  // an empty asm, so that in a loop over tiles neither the work-item id
+  // register nor anything derived from the lane stays live across a tile.
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  asm volatile("" : "+v"(lane));
+  const int tid = w * 64 + lane, lm = lane & 15, g = lane >> 4;
   const HeadView hv = head_view<2, 2>(a, tl.bh);
   const int n = hv.n;
   // n is rarely a multiple of 384: the tiles are laid out from the last row
@@ -1210,9 +1235,9 @@ void fwd_w48(FwdArgs a) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[t][qb] = f32x4_t{};
       }
-      // operand i = (k-step i / KT, sub-tile i % KT), read FA_W48_AHEAD
+      // operand i = (k-step i / KT, sub-tile i % KT), read KA
       // ahead in a pinned order
-      constexpr int NKO = NKS * KT, KA = FA_W48_AHEAD;
+      constexpr int NKO = NKS * KT;
       auto kread = [&](int i) __attribute__((always_inline)) {
         const int ks = i / KT, t = i % KT;
         const int row = 32 * h + krow + 4 * t;
@@ -1393,11 +1418,16 @@ void fwd_w48(FwdArgs a) {
   wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
 
   // epilogue: O = o / l per query (the four lanes of a query hold partial l),
-  // LSE = ln 2 (m + log2 l)
+  // LSE = ln 2 (m + log2 l). The lane index is formed afresh (opaque), so
+  // that the store addresses are not computed before the tile loop and held
+  // across it.
+  int elane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  asm volatile("" : "+v"(elane));
+  const int elm = elane & 15, eg = elane >> 4;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = pair_sum(pair16_sum(lp[qb]));
-    const int row = qw0 + 16 * qb + lm;
+    const int row = qw0 + 16 * qb + elm;
     const float inv = a.o_mult / lt;
     if (row >= 0 && row < n) {
       uint16_t* orow = (uint16_t*)hv.o + (size_t)row * hv.ors;
@@ -1405,9 +1435,57 @@ void fwd_w48(FwdArgs a) {
       for (int dt = 0; dt < NDT; ++dt) {
         const uint32_t x0 = pack2<IN>(o[dt][qb][0] * inv, o[dt][qb][1] * inv);
         const uint32_t x1 = pack2<IN>(o[dt][qb][2] * inv, o[dt][qb][3] * inv);
-        *(u32x2_t*)(orow + 16 * dt + 4 * g) = u32x2_t{x0, x1};
+        *(u32x2_t*)(orow + 16 * dt + 4 * eg) = u32x2_t{x0, x1};
       }
-      if (g == 0 && hv.lse) hv.lse[row] = (m2[qb] + __log2f(lt)) * kLn2;
+      if (eg == 0 && hv.lse) hv.lse[row] = (m2[qb] + __log2f(lt)) * kLn2;
+    }
+  }
+}
+
+// One workgroup per query tile, in the grid order of tile_of_block.
+template <Elt IN, bool CAUSAL>
+__global__ __launch_bounds__(kW48Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_w48(FwdArgs a) {
+  __shared__ W48RingT ring;
+  const int tiles = (a.n + kW48Bq - 1) / kW48Bq;
+  w48_tile<IN, CAUSAL, FA_W48_AHEAD>(a, ring, tile_of_block(blockIdx.x, a.bh, tiles, CAUSAL, kW48Bq));
+}
+
+// Causal tiles packed: plan.bins groups of tiles per head, each workgroup
+// taking group `bin` of plan.heads_seq heads one after another (longest tile
+// first within a head). Under a causal mask tile t reads 384 (t + 1) keys, so
+// one workgroup per tile leaves the last CUs of a launch with the longest
+// tiles; groups of near-equal total length (chosen on the host) finish
+// together. With bh a multiple of 8, the workgroups of an XCD (workgroup i
+// runs on XCD i mod 8) take the same heads: bh / (8 heads_seq) of them at a
+// time, so that few heads' K and V compete for the XCD's L2.
+template <Elt IN>
+__global__ __launch_bounds__(kW48Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_w48_packed(W48Args wa) {
+  __shared__ W48RingT ring;
+  const FwdArgs& a = wa.a;
+  const int nb = wa.plan.bins, hs = wa.plan.heads_seq, pid = blockIdx.x;
+  const int tiles = (a.n + kW48Bq - 1) / kW48Bq;
+  for (int i = 0; i < hs; ++i) {
+    int bh, bin;
+    if ((a.bh & 7) == 0) {
+      const int s = pid >> 3;
+      bh = ((s / nb) * hs + i) * 8 + (pid & 7);
+      bin = s % nb;
+    } else {
+      bh = pid / nb;
+      bin = pid % nb;
+    }
+    for (int t = tiles - 1; t >= 0; --t) {
+      if (wa.plan.bin_of_tile[t] != bin) continue;
+      // the arguments are read through the kernel-argument pointer after an
+      // empty asm, per tile: loaded where the tile uses them rather than
+      // held in scalar registers across the loop
+      uint64_t ka = (uint64_t)(uintptr_t)__builtin_amdgcn_kernarg_segment_ptr();
+      asm volatile("" : "+s"(ka));
+      const __attribute__((address_space(4))) W48Args* kp = (const __attribute__((address_space(4))) W48Args*)ka;
+      w48_tile<IN, true, FA_W48_PACK_AHEAD>(*(const FwdArgs*)&kp->a, ring, TileId{bh, t});
+      __syncthreads();  // every wave is past the ring before the next tile clears it
     }
   }
 }
@@ -1480,6 +1558,60 @@ hipError_t launch_combine_t(const CombineArgs& a, hipStream_t s) {
 }
 
 
+// Groups of causal query tiles for fwd_w48_packed. Tile t of a head costs its
+// 32-key steps, ceil(min(n, 384 (t + 1) - shift) / 32), plus two steps' worth
+// for its Q loads, ring set-up and stores. The groups are the first-fit-
+// decreasing packing at the smallest capacity it fits (binary search), or
+// longest-first onto the least-loaded group where that gives the lower
+// maximum; the same tiles every call for one (n, bins). Returns the largest
+// group's cost (and the total in *total_out).
+long w48_plan(int n, int tiles, int bins, W48Plan& p, long* total_out) {
+  int cost[kW48PlanTiles];
+  long load[256];
+  uint8_t ffd[kW48PlanTiles], lpt[kW48PlanTiles];
+  const int shift = tiles * kW48Bq - n;
+  long total = 0, biggest = 0;
+  for (int t = 0; t < tiles; ++t) {
+    const int keys = std::min(n, kW48Bq * (t + 1) - shift);
+    cost[t] = (keys + kW48Bk - 1) / kW48Bk + 2;
+    total += cost[t];
+    biggest = std::max<long>(biggest, cost[t]);
+  }
+  // cost grows with t: t = tiles - 1 .. 0 is decreasing order
+  auto fits = [&](long cap) {
+    std::fill(load, load + bins, 0L);
+    for (int t = tiles - 1; t >= 0; --t) {
+      int b = 0;
+      while (b < bins && load[b] + cost[t] > cap) ++b;
+      if (b == bins) return false;
+      load[b] += cost[t];
+      ffd[t] = (uint8_t)b;
+    }
+    return true;
+  };
+  long lo = std::max(biggest, (total + bins - 1) / bins), hi = total;
+  while (lo < hi) {
+    const long mid = (lo + hi) / 2;
+    if (fits(mid)) hi = mid;
+    else lo = mid + 1;
+  }
+  fits(lo);
+  std::fill(load, load + bins, 0L);
+  long lpt_max = 0;
+  for (int t = tiles - 1; t >= 0; --t) {
+    const int b = (int)(std::min_element(load, load + bins) - load);
+    load[b] += cost[t];
+    lpt[t] = (uint8_t)b;
+    lpt_max = std::max(lpt_max, load[b]);
+  }
+  const uint8_t* best = lpt_max < lo ? lpt : ffd;
+  p.bins = bins;
+  p.heads_seq = 1;
+  std::copy(best, best + tiles, p.bin_of_tile);
+  *total_out = total;
+  return std::min(lpt_max, lo);
+}
+
 template <Elt E, int D>
 hipError_t dispatch_causal(const FwdArgs& a, hipStream_t s) {
   if constexpr (E == Elt::F32) {
@@ -1490,12 +1622,41 @@ hipError_t dispatch_causal(const FwdArgs& a, hipStream_t s) {
   } else {
     if constexpr (D == 128 && FA_W48 != 0) {
       const int wt = (a.n + kW48Bq - 1) / kW48Bq;
-      // 384-row tiles for long heads (n >= FA_W48_MIN_N), where they measured
-      // faster, and only while they give every CU two or more workgroups;
+      // 384-row tiles only while they give every CU two or more workgroups;
       // ragged batches, split keys and partial outputs stay on the 256-row
       // kernel
-      if (!a.cu_seqlens && a.splits == 1 && !a.part_o && a.n >= FA_W48_MIN_N &&
-          (long)a.bh * wt >= 2L * device_cus()) {
+      const bool dense = !a.cu_seqlens && a.splits == 1 && !a.part_o && (long)a.bh * wt >= 2L * device_cus();
+      // causal heads of FA_W48_PACK_MIN_N <= n < FA_W48_MIN_N: the tiles
+      // packed into groups of near-equal length, one workgroup per group and
+      // at most one per CU, when every head gets two or more groups (longer
+      // heads measured faster with one workgroup per tile, in the order of
+      // tile_of_block: one head at a time per XCD, longest tiles first)
+      const int cus = device_cus(), nb = cus / a.bh;
+      if (FA_W48_PACK && dense && a.causal && a.n >= FA_W48_PACK_MIN_N && a.n < FA_W48_MIN_N &&
+          wt <= kW48PlanTiles && nb >= 2 && nb <= 255) {
+        W48Args wa{};
+        wa.a = a;
+        long total = 0;
+        w48_plan(a.n, wt, nb, wa.plan, &total);
+        // fewer heads at a time per XCD (each workgroup taking 2, 4, ... heads
+        // in turn, with proportionally more groups per head) while the groups
+        // stay within 3% of equal
+        if ((a.bh & 7) == 0) {
+          for (int hs = 2; (a.bh / 8) % hs == 0 && cus * hs / a.bh <= std::min(wt, 255); hs *= 2) {
+            W48Plan p2;
+            const int nb2 = cus * hs / a.bh;
+            const long mx = w48_plan(a.n, wt, nb2, p2, &total);
+            if (mx * nb2 > total + total * 3 / 100) break;
+            p2.heads_seq = hs;
+            wa.plan = p2;
+          }
+        }
+        const unsigned grid = (unsigned)(a.bh / wa.plan.heads_seq * wa.plan.bins);
+        return launch_kernel(fwd_w48_packed<E>, dim3(grid), dim3(kW48Threads), s, wa);
+      }
+      // otherwise one workgroup per tile for long heads (n >= FA_W48_MIN_N),
+      // where that measured faster than the 256-row kernel
+      if (dense && a.n >= FA_W48_MIN_N) {
         const dim3 grid((unsigned)a.bh * (unsigned)wt, 1u);
         return a.causal ? launch_kernel(fwd_w48<E, true>, grid, dim3(kW48Threads), s, a)
                         : launch_kernel(fwd_w48<E, false>, grid, dim3(kW48Threads), s, a);
