@@ -54,7 +54,7 @@ KERNEL_OF_DTYPE = {"bf16": "fwd_direct", "f16": "fwd_direct", "fp8": "fwd_direct
 # <= n < W48_MIN_N on fwd_w48_packed (while every head gets two or more
 # workgroups), heads of n >= W48_MIN_N on fwd_w48; the same rule as the
 # forward dispatch in fa_fwd.hip
-W48_PACK_MIN_N, W48_MIN_N, W48_ROWS = 8192, 16384, 384
+W48_PACK_MIN_N, W48_MIN_N, W48_ROWS = 6144, 16384, 384
 
 
 def fwd_kernel(w, split: bool, ragged: bool = False) -> str:

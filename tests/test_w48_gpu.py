@@ -3,10 +3,10 @@ against the fp64 oracle.
 
 fa_forward runs f16 / bf16 heads of d_k 128 on 48-row-per-wave kernels when
 there are two or more 384-row tiles per compute unit (heads x tiles >= 512
-on a 256-CU device): causal heads of 8192 <= n < 16384 with the tiles packed into groups of near-equal length
-(one workgroup per group; with a multiple of 8 heads, each workgroup may
-take two or more heads in turn), heads of n >= 16384 with one workgroup per
-tile. Tiles are laid out from the last row back, so a ragged n leaves a
+on a 256-CU device): causal heads of 6144 <= n < 16384 with the tiles packed
+into groups of near-equal length (one workgroup per group; with a multiple
+of 8 heads, each workgroup may take two or more heads in turn), heads of
+n >= 16384 with one workgroup per tile. Tiles are laid out from the last row back, so a ragged n leaves a
 partial first tile whose missing rows lie before row 0, and the softmax
 takes no chunk max unless a lane's sum of p passes 2^64 (bf16) or 2^15
 (f16). The shapes below take each path; rows are a seeded sample (the first
@@ -57,6 +57,8 @@ def _dev(t):
     ("f16", True, 12, 16200),     # packed, 21 groups per head (12 heads: no XCD grouping); first tile 72 rows
     ("f16", True, 32, 8192),      # packed, 8 groups per head, one head per workgroup
     ("bf16", True, 64, 8200),     # packed, 8 groups per head, two heads in turn; first tile 136 rows
+    ("bf16", True, 32, 6144),     # packed, 16 full tiles in 8 groups of two
+    ("f16", True, 32, 7000),      # packed, 19 tiles; first tile holds 88 rows
 ])
 def test_w48_sampled_rows(dtype, causal, heads, n):
     say(f"w48 [1, {heads}, {n}, {D}] {dtype} causal={causal}")

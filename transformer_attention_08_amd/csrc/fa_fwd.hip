@@ -1032,7 +1032,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 #define FA_W48_PACK_AHEAD 4  // the same, packed causal tiles
 #endif
 #ifndef FA_W48_PACK_MIN_N
-#define FA_W48_PACK_MIN_N 8192
+#define FA_W48_PACK_MIN_N 6144
 #endif
 #ifndef FA_W48_MIN_N
 #define FA_W48_MIN_N 16384
