@@ -1004,8 +1004,8 @@ void fwd_mfma32(FwdArgs a) {
 // from LDS feeds the MFMAs of the wave's three 16-row query blocks, and every
 // key tile copied into LDS serves 384 query rows (fwd_direct: one MFMA per
 // operand read, 256 rows per tile), so both the LDS operand reads and the
-// L2 -> LDS copies per FLOP are a third lower. 32-key tiles in a 6-slot ring
-// (96 KiB), one workgroup barrier per two tiles.
+// L2 -> LDS copies per FLOP are a third lower. 32-key tiles in a 9-slot ring
+// (144 KiB), one workgroup barrier per three tiles.
 //
 // 16x16x32 operand layouts: A, lane l: row l % 16, k-elements 8(l/16)..+7;
 // B, lane l: column l % 16, k-elements 8(l/16)..+7; accumulator, lane l:
@@ -1023,7 +1023,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 #define FA_W48 1
 #endif
 #ifndef FA_W48_STAGES
-#define FA_W48_STAGES 6
+#define FA_W48_STAGES 9
 #endif
 #ifndef FA_W48_AHEAD
 #define FA_W48_AHEAD 3  // K operands read ahead, one workgroup per tile
@@ -1038,7 +1038,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 #define FA_W48_MIN_N 16384
 #endif
 #ifndef FA_W48_GROUP
-#define FA_W48_GROUP 2  // key tiles per workgroup barrier (1, 2 or 3; the ring has 3x as many slots)
+#define FA_W48_GROUP 3  // key tiles per workgroup barrier (1, 2 or 3; the ring has 3x as many slots)
 #endif
 #ifndef FA_W48_PRIO
 #define FA_W48_PRIO 1
@@ -1108,6 +1108,7 @@ struct W48Ring {
 struct SlotView {
   uint8_t* k;
   uint8_t* v;
+  int off;  // the slot's byte offset within the K (and the V) array
 };
 
 __device__ inline int w48_kswz(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
@@ -1204,6 +1205,30 @@ __device__ __attribute__((always_inline)) inline void w48_tile(const FwdArgs& a,
   const int vrow = 8 * g + (lm >> 2);
   const int vsw = 2 * ((lm >> 2) | ((g & 1) << 2));
   const int vch = (lm & 3) >> 1, vhalf = (lm & 1) * 8;
+  // LDS read addresses per K k-step and per V d-tile, relative to the start
+  // of each array and formed once: a slot's and a sub-tile's offsets then
+  // fit the reads' 16-bit immediates (each array spans 48 KiB), instead of
+  // one set of address registers per slot. The empty asm hides their
+  // origin; the mask after it tells the compiler the sign bit is clear,
+  // which lets it fold the immediates.
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  uint32_t kad[NKS], vad[NDT];
+  {
+    const uint32_t kb = (uint32_t)(uintptr_t)(lds_u8*)&ring.k[0][0];
+    const uint32_t vb = (uint32_t)(uintptr_t)(lds_u8*)&ring.v[0][0];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      kad[ks] = kb + krow * ROWB + (((4 * ks + g) ^ lm) * 16);
+      asm volatile("" : "+v"(kad[ks]));
+      kad[ks] &= 0x3ffffu;
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      vad[dt] = vb + vrow * ROWB + (((2 * dt + vch) ^ vsw) * 16) + vhalf;
+      asm volatile("" : "+v"(vad[dt]));
+      vad[dt] &= 0x3ffffu;
+    }
+  }
 
   const float c = a.c;
   float m2[QB], lp[QB];
@@ -1241,7 +1266,8 @@ __device__ __attribute__((always_inline)) inline void w48_tile(const FwdArgs& a,
       auto kread = [&](int i) __attribute__((always_inline)) {
         const int ks = i / KT, t = i % KT;
         const int row = 32 * h + krow + 4 * t;
-        return *(const u32x4_t*)(slot.k + row * ROWB + (((4 * ks + g) ^ lm) * 16));
+        return *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(kad[ks] + slot.off +
+                                                                             (row - krow) * ROWB);
       };
       u32x4_t kf[KA];
 #pragma unroll
@@ -1329,9 +1355,11 @@ __device__ __attribute__((always_inline)) inline void w48_tile(const FwdArgs& a,
       // O^T += V^T P^T: per d-tile one V^T operand (two transposing reads of
       // four keys each), three MFMAs
       auto vread = [&](int dt) __attribute__((always_inline)) {
-        const uint8_t* p0 = slot.v + (32 * h + vrow) * ROWB + (((2 * dt + vch) ^ vsw) * 16) + vhalf;
-        const u32x2_t lo = lds_read_tr16(p0);
-        const u32x2_t hi = lds_read_tr16(p0 + 4 * ROWB);
+        const uint32_t a0 = vad[dt] + slot.off + 32 * h * ROWB;
+        const u32x2_t lo = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(uintptr_t)a0));
+        const u32x2_t hi = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(uintptr_t)(a0 + 4 * ROWB)));
         return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
       };
       u32x4_t vf[KA];
@@ -1350,7 +1378,7 @@ __device__ __attribute__((always_inline)) inline void w48_tile(const FwdArgs& a,
   };
 
   auto slot_ref = [&](auto S) __attribute__((always_inline)) -> SlotView {
-    return SlotView{ring.k[decltype(S)::value], ring.v[decltype(S)::value]};
+    return SlotView{ring.k[decltype(S)::value], ring.v[decltype(S)::value], decltype(S)::value * TILE_B};
   };
 #if FA_W48_GROUP > 1
   // One barrier per group of GB tiles (NS = 3 GB slots): at a group's first
