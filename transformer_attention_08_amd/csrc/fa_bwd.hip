@@ -399,6 +399,20 @@ struct QSlot {
   __attribute__((aligned(1024))) float st[512];
 };
 
+// The ring of the two-wave dK/dV kernel as three arrays of four slots.
+template <int BYTES>
+struct KvRing {
+  __attribute__((aligned(1024))) uint8_t q[4][BYTES];
+  __attribute__((aligned(1024))) uint8_t g[4][BYTES];
+  __attribute__((aligned(1024))) float st[4][512];
+};
+struct QView {
+  uint8_t* q;
+  uint8_t* g;
+  float* st;
+  int off;  // the slot's byte offset within the q (and the g) array
+};
+
 template <Elt IN, int D, bool CAUSAL>
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv(BwdArgs a) {
@@ -658,7 +672,11 @@ void bwd_dkdv2(BwdArgs a) {
   static_assert(LPW >= 1, "tile too small for the wave count");
   static_assert(kKvBk == 4 * 32, "four key blocks of 32 per workgroup");
 
-  __shared__ QSlot<TILE_B> ring0, ring1, ring2, ring3;
+  // Q tiles, dO tiles and their row statistics in three arrays, so that
+  // every read of a slot is a lane base register plus an immediate below
+  // 64 KiB (with one QSlot per slot the compiler held address registers per
+  // slot)
+  __shared__ KvRing<TILE_B> kr;
   // P of the current tile: [register half][key block][query block][lane]
   __shared__ u32x4_t pbuf[2][4][QB][64];
 
@@ -690,7 +708,7 @@ void bwd_dkdv2(BwdArgs a) {
     const int row = byte / ROWB, p = (byte % ROWB) / 16;
     off[i] = (uint32_t)row * hv.rs + (uint32_t)((p ^ swz2<D>(row)) * 16);
   }
-  auto issue = [&](QSlot<TILE_B>& slot, int t) __attribute__((always_inline)) {
+  auto issue = [&](const QView& slot, int t) __attribute__((always_inline)) {
     const bool in = t < nt;
     const uint32_t base = in ? (uint32_t)(t * kKvBq) * hv.rs : 0x80000000u;
     const uint32_t sbase = in ? (uint32_t)t * (kKvBq * 4) : 0x80000000u;
@@ -724,13 +742,16 @@ void bwd_dkdv2(BwdArgs a) {
   // lane's key fragments F (K or V). The MFMAs alternate between the blocks
   // (two independent accumulators); operand i (block i % QB, k-step i / QB)
   // is read FA_BWD_SDP_AHEAD MFMAs ahead in a pinned order.
-  auto prod = [&](const uint8_t* x, const u32x4_t (&f)[NKS], f32x16_t (&acc)[QB]) __attribute__((always_inline)) {
+  // lb[ks]: this lane's read address for k-step ks in slot 0 of the array
+  auto prod = [&](const uint32_t (&lb)[NKS], int off, const u32x4_t (&f)[NKS], f32x16_t (&acc)[QB])
+                  __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) acc[qb] = f32x16_t{};
     constexpr int NOP = QB * NKS, PA = FA_BWD_SDP_AHEAD < NOP ? FA_BWD_SDP_AHEAD : NOP;
     auto rd_ = [&](int i) __attribute__((always_inline)) {
-      const int row = (i % QB) * 32 + qr, ks = i / QB;
-      return *(const u32x4_t*)(x + row * ROWB + (((2 * ks + hl) ^ sw_r) * 16));
+      const int ks = i / QB;
+      return *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(lb[ks] + off +
+                                                                          (i % QB) * 32 * ROWB);
     };
     u32x4_t buf[PA];
 #pragma unroll
@@ -744,26 +765,27 @@ void bwd_dkdv2(BwdArgs a) {
   };
   // acc[db] += X^T B over the 32 queries of block qb: X^T (dO^T or Q^T) from
   // transposing reads, B (P or dS, 16 queries per half) from registers.
-  auto prod_t = [&](const uint8_t* x, int qb, const u32x4_t (&b)[2], f32x16_t (&acc)[NDB]) __attribute__((always_inline)) {
+  // tb[db][0 / 1]: this lane's addresses of the two transposing reads of
+  // d-block db in slot 0 of the array
+  auto prod_t = [&](const uint32_t (&tb)[NDB][2], int off, int qb, const u32x4_t (&b)[2], f32x16_t (&acc)[NDB])
+                    __attribute__((always_inline)) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int r = qb * 32 + 16 * s2 + trow;
-        const int col = db * 32 + tcol;
-        const int half = (col & 4) << 1;
-        const u32x2_t lo = lds_read_tr16(x + r * ROWB + (((col >> 3) ^ sw_lo) * 16) + half);
-        const u32x2_t hi = lds_read_tr16(x + (r + 4) * ROWB + (((col >> 3) ^ sw_hi) * 16) + half);
+        const int rr = off + (qb * 32 + 16 * s2) * ROWB;
+        const u32x2_t lo = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(uintptr_t)(tb[db][0] + rr)));
+        const u32x2_t hi = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(uintptr_t)(tb[db][1] + rr)));
         acc[db] = mfma16<IN>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, b[s2], acc[db]);
       }
     }
   };
 
-  auto slot_ref = [&](auto S) __attribute__((always_inline)) -> QSlot<TILE_B>& {
-    if constexpr (decltype(S)::value == 0) return ring0;
-    else if constexpr (decltype(S)::value == 1) return ring1;
-    else if constexpr (decltype(S)::value == 2) return ring2;
-    else return ring3;
+  auto slot_ref = [&](auto S) __attribute__((always_inline)) -> QView {
+    constexpr int sv = decltype(S)::value;
+    return QView{kr.q[sv], kr.g[sv], kr.st[sv], sv * TILE_B};
   };
 
   // The two roles run separate copies of the tile loop with the same
@@ -777,22 +799,46 @@ void bwd_dkdv2(BwdArgs a) {
       for (int ks = 0; ks < NKS; ++ks) f[ks] = bload16(rf, (uint32_t)key * hv.rs + (ks * 16 + hl * 8) * 2);
     }
     wait_vmcnt<0>();
+    // lane base addresses: lbx for the row-wise reads (Q for the S waves,
+    // dO for the dP waves), tby for the transposing reads (dO, resp. Q); the
+    // empty asm hides their origin and the mask tells the compiler the sign
+    // bit is clear, so that slot and block offsets fold into immediates
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    uint32_t lbx[NKS], tby[NDB][2];
+    {
+      const uint32_t xa = (uint32_t)(uintptr_t)(lds_u8*)(kS ? &kr.q[0][0] : &kr.g[0][0]);
+      const uint32_t ya = (uint32_t)(uintptr_t)(lds_u8*)(kS ? &kr.g[0][0] : &kr.q[0][0]);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        lbx[ks] = xa + qr * ROWB + (((2 * ks + hl) ^ sw_r) * 16);
+        asm volatile("" : "+v"(lbx[ks]));
+        lbx[ks] &= 0x3ffffu;
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int col = db * 32 + tcol;
+        const int half = (col & 4) << 1;
+        tby[db][0] = ya + trow * ROWB + (((col >> 3) ^ sw_lo) * 16) + half;
+        tby[db][1] = ya + (trow + 4) * ROWB + (((col >> 3) ^ sw_hi) * 16) + half;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          asm volatile("" : "+v"(tby[db][e]));
+          tby[db][e] &= 0x3ffffu;
+        }
+      }
+    }
     f32x16_t acc[NDB];  // dV (kS) or dK
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
 
     {
-      QSlot<TILE_B>* slots[4] = {&ring0, &ring1, &ring2, &ring3};
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        u32x4_t* p = (u32x4_t*)slots[s];
-        for (int i = tid; i < (int)(sizeof(QSlot<TILE_B>) / 16); i += kKv2Threads) p[i] = u32x4_t{0, 0, 0, 0};
-      }
+      u32x4_t* p = (u32x4_t*)&kr;
+      for (int i = tid; i < (int)(sizeof(kr) / 16); i += kKv2Threads) p[i] = u32x4_t{0, 0, 0, 0};
     }
     __syncthreads();
-    issue(ring0, i_lo);
-    if constexpr (NS > 2) issue(ring1, i_lo + 1);
-    if constexpr (NS > 3) issue(ring2, i_lo + 2);
+    issue(slot_ref(std::integral_constant<int, 0>{}), i_lo);
+    if constexpr (NS > 2) issue(slot_ref(std::integral_constant<int, 1>{}), i_lo + 1);
+    if constexpr (NS > 3) issue(slot_ref(std::integral_constant<int, 2>{}), i_lo + 2);
 
     // dS of the previous tile and whether that tile was live (dS waves): its
     // dK product runs in the next step, beside the S waves' exponentials.
@@ -805,13 +851,13 @@ void bwd_dkdv2(BwdArgs a) {
 #if !FA_BWD_LAG
       issue(slot_ref(SN{}), it + NS - 1);
 #endif
-      const QSlot<TILE_B>& slot = slot_ref(S);
+      const QView slot = slot_ref(S);
       const bool lv = live(it);
       if constexpr (kS) {
         u32x4_t pb[QB][2];
         if (lv) {
           f32x16_t sv[QB];
-          prod(slot.q, f, sv);
+          prod(lbx, slot.off, f, sv);
           const bool mask = needs_mask(it);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
@@ -849,7 +895,7 @@ void bwd_dkdv2(BwdArgs a) {
 #endif
         if (lv) {
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) prod_t(slot.g, qb, pb[qb], acc);  // dV^T += dO^T P
+          for (int qb = 0; qb < QB; ++qb) prod_t(tby, slot.off, qb, pb[qb], acc);  // dV^T += dO^T P
         }
       } else {
         f32x16_t dp[QB];
@@ -858,10 +904,10 @@ void bwd_dkdv2(BwdArgs a) {
         // after the next barrier
         if (pl) {
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) prod_t(slot_ref(SN{}).q, qb, dsp[qb], acc);
+          for (int qb = 0; qb < QB; ++qb) prod_t(tby, slot_ref(SN{}).off, qb, dsp[qb], acc);
         }
 #endif
-        if (lv) prod(slot.g, f, dp);
+        if (lv) prod(lbx, slot.off, f, dp);
         __syncthreads();  // P is in LDS
 #if FA_BWD_LAG
         issue(slot_ref(SN{}), it + NS - 1);
@@ -891,7 +937,7 @@ void bwd_dkdv2(BwdArgs a) {
             dsp[qb][0] = dsb[0];
             dsp[qb][1] = dsb[1];
 #else
-            prod_t(slot.q, qb, dsb, acc);  // dK^T += Q^T dS
+            prod_t(tby, slot.off, qb, dsb, acc);  // dK^T += Q^T dS
 #endif
           }
         }
@@ -909,9 +955,8 @@ void bwd_dkdv2(BwdArgs a) {
     if constexpr (!kS) {
       if (pl) {  // the last tile's dK product (no copy targets its slot any more)
         const int ls = (nt - 1 - i_lo) % NS;
-        const uint8_t* lq = ls == 0 ? ring0.q : ls == 1 ? ring1.q : ls == 2 ? ring2.q : ring3.q;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) prod_t(lq, qb, dsp[qb], acc);
+        for (int qb = 0; qb < QB; ++qb) prod_t(tby, ls * TILE_B, qb, dsp[qb], acc);
       }
     }
 #endif
