@@ -281,6 +281,60 @@ __device__ inline void pv_tile(f32x16_t (&o)[NDB], const uint8_t* v, int vrow0, 
 #endif
 }
 
+// qk_tile and pv_tile with the LDS reads addressed from lane base registers
+// (slot 0 of a K or V array: kbase[ks] for the K operand of k-step ks,
+// vbase[db] for the first transposing read of d-block db) plus the slot's
+// offset and the block offsets as immediates; the same reads in the same
+// order.
+template <Elt IN, int KB, int NKS, int ROWB>
+__device__ inline void qk_tile_b(f32x16_t (&s)[KB], const uint32_t (&kbase)[NKS], int off,
+                                 const u32x4_t (&qf)[NKS]) {
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16_t{};
+  auto kread = [&](int i) __attribute__((always_inline)) {
+    const int ks = i / KB, kb = i % KB;
+    return *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(kbase[ks] + off + kb * 32 * ROWB);
+  };
+  constexpr int NQ = NKS * KB, PA = FA_QK_AHEAD > 0 ? (FA_QK_AHEAD < NQ ? FA_QK_AHEAD : NQ) : 1;
+  u32x4_t kf[PA];
+#pragma unroll
+  for (int i = 0; i < PA; ++i) kf[i] = kread(i);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    s[i % KB] = mfma16<IN>(kf[i % PA], qf[i / KB], s[i % KB]);
+    if (i + PA < NQ) kf[i % PA] = kread(i + PA);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <Elt IN, int KB, int NDB, int ROWB>
+__device__ inline void pv_tile_b(f32x16_t (&o)[NDB], const uint32_t (&vbase)[NDB], int off,
+                                 const u32x4_t (&pb)[KB][2]) {
+  auto vread = [&](int i) __attribute__((always_inline)) -> u32x4_t {
+    const int kb = i / (2 * NDB), s2 = (i / NDB) % 2, db = i % NDB;
+    const uint32_t a0 = vbase[db] + off + (kb * 32 + 16 * s2) * ROWB;
+    const u32x2_t lo = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)(uintptr_t)a0));
+    const u32x2_t hi = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)(uintptr_t)(a0 + 4 * ROWB)));
+    return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+  };
+  constexpr int NPV = KB * 2 * NDB;
+  constexpr int PA = FA_PV_AHEAD > 0 ? (FA_PV_AHEAD < NPV ? FA_PV_AHEAD : NPV) : 1;
+  u32x4_t vf[PA];
+#pragma unroll
+  for (int i = 0; i < PA; ++i) vf[i] = vread(i);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) {
+    const int kb = i / (2 * NDB), s2 = (i / NDB) % 2, db = i % NDB;
+    o[db] = mfma16<IN>(vf[i % PA], pb[kb][s2], o[db]);
+    if (i + PA < NPV) vf[i % PA] = vread(i + PA);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Epilogue store of one wave's 32 rows of O through LDS. The O^T
 // accumulator holds one query row per lane, so storing it directly writes 32
 // rows, 16 bytes each, per store instruction; at the end of a query tile the
@@ -348,6 +402,20 @@ struct LdsSlot {
   __attribute__((aligned(1024))) uint8_t v[BYTES];
 };
 
+// The K/V ring of fwd_direct as two arrays of NSL slots, so that each array
+// (64 KiB at most) is reached from one set of lane base registers with the
+// slot and block offsets as immediates.
+template <int BYTES, int NSL>
+struct DirectRing {
+  __attribute__((aligned(1024))) uint8_t k[NSL][BYTES];
+  __attribute__((aligned(1024))) uint8_t v[NSL][BYTES];
+};
+struct RingView {
+  uint8_t* k;
+  uint8_t* v;
+  int off;  // the slot's byte offset within each array
+};
+
 template <Elt IN, int D, bool CAUSAL>
 __global__ __launch_bounds__(kDirectThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_direct(FwdArgs a) {
@@ -358,7 +426,7 @@ void fwd_direct(FwdArgs a) {
   constexpr int NKS = D / 16;          // MFMA k-steps of Q K^T
   constexpr int NDB = D / 32;          // 32-column blocks of O
 
-  __shared__ LdsSlot<TILE_B> ring0, ring1, ring2, ring3;
+  __shared__ DirectRing<TILE_B, NS> dr;
   static_assert(NS >= 2 && NS <= 4, "stages");
 
   const int tid = threadIdx.x;
@@ -402,7 +470,7 @@ void fwd_direct(FwdArgs a) {
   // so every step issues the same number of loads. The copies are issued
   // through inline assembly: the compiler does not track them, and the
   // explicit vmcnt wait plus barrier in each step orders them.
-  auto issue = [&](LdsSlot<TILE_B>& slot, int J) __attribute__((always_inline)) {
+  auto issue = [&](const RingView& slot, int J) __attribute__((always_inline)) {
     const int t = pair && J >= nt0 ? J - nt0 : J;
     const uint32_t kb = J < nt ? (uint32_t)(t * BK) * hv.krs : 0x80000000u;
     const uint32_t vb = J < nt ? (uint32_t)(t * BK) * hv.vrs : 0x80000000u;
@@ -437,6 +505,28 @@ void fwd_direct(FwdArgs a) {
   const int vrow0 = 8 * hl + (li >> 2);                 // + kb*32 + 16*s2 + 4*r
   const int vswz = L::vswz(vrow0);
   const int vcol = 16 * (grp & 1) + 4 * (li & 3);       // + db*32 (d-column of the 8-byte chunk)
+  // the read addresses of slot 0 (K: per k-step; V: per d-block), hidden
+  // from the compiler behind an empty asm, the mask telling it the sign bit
+  // is clear, so that slot and block offsets fold into immediates
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  uint32_t kbase[NKS], vbase[NDB];
+  {
+    const uint32_t ka = (uint32_t)(uintptr_t)(lds_u8*)&dr.k[0][0];
+    const uint32_t va = (uint32_t)(uintptr_t)(lds_u8*)&dr.v[0][0];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      kbase[ks] = ka + krow * ROWB + (((2 * ks + hl) ^ kswz) * 16);
+      asm volatile("" : "+v"(kbase[ks]));
+      kbase[ks] &= 0x3ffffu;
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int col = db * 32 + vcol;
+      vbase[db] = va + vrow0 * ROWB + (((col >> 3) ^ vswz) * 16) + ((col & 4) << 1);
+      asm volatile("" : "+v"(vbase[db]));
+      vbase[db] &= 0x3ffffu;
+    }
+  }
 
   const float c = a.c;
   float m2 = -INFINITY, lp = 0.f;
@@ -446,10 +536,10 @@ void fwd_direct(FwdArgs a) {
   auto live = [&](int j) __attribute__((always_inline)) { return qw0 < n && !(CAUSAL && j * BK > qw0 + 31); };
   auto needs_mask = [&](int j) __attribute__((always_inline)) { return (j * BK + BK > n) || (CAUSAL && j * BK + BK - 1 > qw0); };
 
-  auto compute = [&](const LdsSlot<TILE_B>& slot, int j, auto&& mid) __attribute__((always_inline)) {
+  auto compute = [&](const RingView& slot, int j, auto&& mid) __attribute__((always_inline)) {
     // S^T = K Q^T
     f32x16_t s[KB];
-    qk_tile<IN, KB, NKS, ROWB>(s, slot.k, krow, kswz, hl, qf);
+    qk_tile_b<IN, KB, NKS, ROWB>(s, kbase, slot.off, qf);
     if (needs_mask(j)) {
       // register i of key block kb holds key j*BK + 8*hl + off with
       // off = kb*32 + 16*(i >> 3) + (i & 7), a constant: the key is visible
@@ -502,20 +592,18 @@ void fwd_direct(FwdArgs a) {
     // the next tile's copies go out here, between the softmax and P.V (see step)
     mid();
     // O^T += V^T P^T; consecutive MFMAs go to different accumulators
-    pv_tile<IN, KB, NDB, ROWB>(o, slot.v, vrow0, vcol, vswz, pb);
+    pv_tile_b<IN, KB, NDB, ROWB>(o, vbase, slot.off, pb);
   };
 
-  auto slot_ref = [&](auto S) __attribute__((always_inline)) -> LdsSlot<TILE_B>& {
-    if constexpr (decltype(S)::value == 0) return ring0;
-    else if constexpr (decltype(S)::value == 1) return ring1;
-    else if constexpr (decltype(S)::value == 2) return ring2;
-    else return ring3;
+  auto slot_ref = [&](auto S) __attribute__((always_inline)) -> RingView {
+    constexpr int sv = decltype(S)::value;
+    return RingView{dr.k[sv], dr.v[sv], sv * TILE_B};
   };
   // Epilogue of a query tile: O = o / l once per row; LSE = ln 2 * (m2 + log2 l).
   // O goes out through `stage`, a ring slot no wave reads any more once every
   // wave has passed the barrier here (the copies in flight fill the other
   // slot).
-  auto finish = [&](uint8_t* stage) __attribute__((always_inline)) {
+  auto finish = [&](const RingView& slot) __attribute__((always_inline)) {
     const float lt = pair_sum(lp);
     if (a.part_o) {
       if (qrow < n) store_partial<NDB>(a, tl.bh, qrow, hl, o, m2, lt);
@@ -523,9 +611,13 @@ void fwd_direct(FwdArgs a) {
       const float inv = a.o_mult / lt;
       // the staged rows of all waves must fit in one ring slot (64-key tiles
       // at d_k 128 leave a 32 KiB slot for 64 KiB of rows: store directly)
-      if constexpr (sizeof(LdsSlot<TILE_B>) >= (size_t)kDirectWaves * 32 * ROWB) {
+      if constexpr (2 * TILE_B >= kDirectWaves * 32 * ROWB) {
         __syncthreads();
-        store_o_staged<IN, NDB>(stage + w * 32 * ROWB, lr, hl, lane, o, inv,
+        // the slot's K tile, then its V tile, as one staging area of
+        // 32-row blocks (a tile holds a whole number of blocks)
+        const int sb = w * 32 * ROWB;
+        uint8_t* stage = sb < TILE_B ? slot.k + sb : slot.v + (sb - TILE_B);
+        store_o_staged<IN, NDB>(stage, lr, hl, lane, o, inv,
                                 (uint16_t*)hv.o + (size_t)qw0 * hv.ors, hv.ors, n - qw0);
       } else {
         if (qrow < n) store_o_row<IN, NDB>((uint16_t*)hv.o + (size_t)qrow * hv.ors, hl, o, inv);
@@ -569,20 +661,15 @@ void fwd_direct(FwdArgs a) {
   // Zero the ring once, so that rows a load leaves unwritten can never hold
   // NaN patterns (P is 0 there, but 0 * NaN is NaN).
   {
-    LdsSlot<TILE_B>* slots[4] = {&ring0, &ring1, &ring2, &ring3};
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      u32x4_t* p = (u32x4_t*)slots[s];
-      for (int i = tid; i < (int)(sizeof(LdsSlot<TILE_B>) / 16); i += kDirectThreads)
-        p[i] = u32x4_t{0, 0, 0, 0};
-    }
+    u32x4_t* p = (u32x4_t*)&dr;
+    for (int i = tid; i < (int)(sizeof(dr) / 16); i += kDirectThreads) p[i] = u32x4_t{0, 0, 0, 0};
   }
   __syncthreads();
 
   // prologue: tiles j_lo .. j_lo + NS - 2
-  issue(ring0, j_lo);
-  if constexpr (NS > 2) issue(ring1, j_lo + 1);
-  if constexpr (NS > 3) issue(ring2, j_lo + 2);
+  issue(slot_ref(std::integral_constant<int, 0>{}), j_lo);
+  if constexpr (NS > 2) issue(slot_ref(std::integral_constant<int, 1>{}), j_lo + 1);
+  if constexpr (NS > 3) issue(slot_ref(std::integral_constant<int, 2>{}), j_lo + 2);
 
   run(j_lo, nt0, 0);
   if (pair) {
@@ -592,7 +679,10 @@ void fwd_direct(FwdArgs a) {
     // their latency overlaps it; the next step waits for them and the keys.
     // The slot of the first tile's last position is free for O.
     load_q(tl.t * kDirectBq + 32 * w + lr);
-    finish(((nt0 - 1 - j_lo) & 1) ? (uint8_t*)&ring1 : (uint8_t*)&ring0);
+    {
+      const int fs = (nt0 - 1 - j_lo) & 1;
+      finish(RingView{dr.k[fs], dr.v[fs], fs * TILE_B});
+    }
     q0 = tl.t * kDirectBq;
     qw0 = q0 + 32 * w;
     qrow = qw0 + lr;
@@ -603,7 +693,7 @@ void fwd_direct(FwdArgs a) {
     run(nt0, nt, nt0);
   }
   wait_vmcnt<0>();  // no load may still be writing LDS (nor may when the workgroup ends)
-  finish((uint8_t*)&ring0);
+  finish(slot_ref(std::integral_constant<int, 0>{}));
 }
 
 // ---------------------------------------------------------------------------
