@@ -206,89 +206,16 @@ constexpr int kDirectBq = 32 * kDirectWaves;
 
 // S^T = K Q^T for one key tile: KB accumulators of 32 keys, NKS k-steps.
 // K is read from its swizzled LDS tile (row kb * 32 + krow, 16-byte chunk
-// 2 ks + hl of the row, XOR kswz); Q is the register-held B operand. With
-// FA_QK_AHEAD > 0 the K operands are read that many MFMAs ahead in a fixed
+// 2 ks + hl of the row, XOR kswz); Q is the register-held B operand. The
+// reads take lane base registers, kbase[ks] = this lane's address of k-step
+// ks in slot 0 of the K array, plus the slot's offset and kb * 32 rows as
+// immediates. The K operands are read FA_QK_AHEAD MFMAs ahead in a fixed
 // order (operand i, i.e. k-step i / KB of key block i % KB, feeds MFMA i, and
 // the read of operand i + FA_QK_AHEAD goes out right after MFMA i), so that
 // LDS latency hides behind the MFMAs already issued.
 template <Elt IN, int KB, int NKS, int ROWB>
-__device__ inline void qk_tile(f32x16_t (&s)[KB], const uint8_t* k, int krow, int kswz, int hl,
+__device__ inline void qk_tile(f32x16_t (&s)[KB], const uint32_t (&kbase)[NKS], int off,
                                const u32x4_t (&qf)[NKS]) {
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16_t{};
-  auto kaddr = [&](int i) __attribute__((always_inline)) {
-    const int ks = i / KB, kb = i % KB;
-    return (const u32x4_t*)(k + (kb * 32 + krow) * ROWB + (((2 * ks + hl) ^ kswz) * 16));
-  };
-#if FA_QK_AHEAD > 0
-  constexpr int NQ = NKS * KB, PA = FA_QK_AHEAD < NQ ? FA_QK_AHEAD : NQ;
-  u32x4_t kf[PA];
-#pragma unroll
-  for (int i = 0; i < PA; ++i) kf[i] = *kaddr(i);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < NQ; ++i) {
-    s[i % KB] = mfma16<IN>(kf[i % PA], qf[i / KB], s[i % KB]);
-    if (i + PA < NQ) kf[i % PA] = *kaddr(i + PA);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-#else
-#pragma unroll
-  for (int i = 0; i < NKS * KB; ++i) s[i % KB] = mfma16<IN>(*kaddr(i), qf[i / KB], s[i % KB]);
-#endif
-}
-
-// O^T += V^T P^T for one key tile: for each 32-key block kb, 16-key half s2
-// and 32-column block db, the V^T operand (eight consecutive keys at one
-// d-column per lane) comes from two transposing LDS reads of the swizzled V
-// tile, and P^T (packed 16-bit p) is the register-held B operand. With
-// FA_PV_AHEAD > 0 the V^T operands are read that many MFMAs ahead in a fixed
-// order, the read of operand i + FA_PV_AHEAD issued right after MFMA i, so
-// that the latency of the transposing reads hides behind the MFMAs already
-// issued.
-template <Elt IN, int KB, int NDB, int ROWB>
-__device__ inline void pv_tile(f32x16_t (&o)[NDB], const uint8_t* v, int vrow0, int vcol, int vswz,
-                               const u32x4_t (&pb)[KB][2]) {
-  auto vread = [&](int i) __attribute__((always_inline)) -> u32x4_t {
-    const int kb = i / (2 * NDB), s2 = (i / NDB) % 2, db = i % NDB;
-    const int row = kb * 32 + 16 * s2 + vrow0;
-    const int col = db * 32 + vcol;
-    const uint8_t* p0 = v + row * ROWB + (((col >> 3) ^ vswz) * 16) + ((col & 4) << 1);
-    const u32x2_t lo = lds_read_tr16(p0);
-    const u32x2_t hi = lds_read_tr16(p0 + 4 * ROWB);
-    return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-  };
-  constexpr int NPV = KB * 2 * NDB;
-#if FA_PV_AHEAD > 0
-  constexpr int PA = FA_PV_AHEAD < NPV ? FA_PV_AHEAD : NPV;
-  u32x4_t vf[PA];
-#pragma unroll
-  for (int i = 0; i < PA; ++i) vf[i] = vread(i);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < NPV; ++i) {
-    const int kb = i / (2 * NDB), s2 = (i / NDB) % 2, db = i % NDB;
-    o[db] = mfma16<IN>(vf[i % PA], pb[kb][s2], o[db]);
-    if (i + PA < NPV) vf[i % PA] = vread(i + PA);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-#else
-#pragma unroll
-  for (int i = 0; i < NPV; ++i) {
-    const int kb = i / (2 * NDB), s2 = (i / NDB) % 2, db = i % NDB;
-    o[db] = mfma16<IN>(vread(i), pb[kb][s2], o[db]);
-  }
-#endif
-}
-
-// qk_tile and pv_tile with the LDS reads addressed from lane base registers
-// (slot 0 of a K or V array: kbase[ks] for the K operand of k-step ks,
-// vbase[db] for the first transposing read of d-block db) plus the slot's
-// offset and the block offsets as immediates; the same reads in the same
-// order.
-template <Elt IN, int KB, int NKS, int ROWB>
-__device__ inline void qk_tile_b(f32x16_t (&s)[KB], const uint32_t (&kbase)[NKS], int off,
-                                 const u32x4_t (&qf)[NKS]) {
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16_t{};
   auto kread = [&](int i) __attribute__((always_inline)) {
@@ -308,9 +235,19 @@ __device__ inline void qk_tile_b(f32x16_t (&s)[KB], const uint32_t (&kbase)[NKS]
   }
 }
 
+// O^T += V^T P^T for one key tile: for each 32-key block kb, 16-key half s2
+// and 32-column block db, the V^T operand (eight consecutive keys at one
+// d-column per lane) comes from two transposing LDS reads of the swizzled V
+// tile, and P^T (packed 16-bit p) is the register-held B operand. The reads
+// take lane base registers, vbase[db] = this lane's address of the first
+// read of d-block db in slot 0 of the V array, plus the slot's offset and
+// the row offsets as immediates. The V^T operands are read FA_PV_AHEAD MFMAs
+// ahead in a fixed order, the read of operand i + FA_PV_AHEAD issued right
+// after MFMA i, so that the latency of the transposing reads hides behind the
+// MFMAs already issued.
 template <Elt IN, int KB, int NDB, int ROWB>
-__device__ inline void pv_tile_b(f32x16_t (&o)[NDB], const uint32_t (&vbase)[NDB], int off,
-                                 const u32x4_t (&pb)[KB][2]) {
+__device__ inline void pv_tile(f32x16_t (&o)[NDB], const uint32_t (&vbase)[NDB], int off,
+                               const u32x4_t (&pb)[KB][2]) {
   auto vread = [&](int i) __attribute__((always_inline)) -> u32x4_t {
     const int kb = i / (2 * NDB), s2 = (i / NDB) % 2, db = i % NDB;
     const uint32_t a0 = vbase[db] + off + (kb * 32 + 16 * s2) * ROWB;
@@ -539,7 +476,7 @@ void fwd_direct(FwdArgs a) {
   auto compute = [&](const RingView& slot, int j, auto&& mid) __attribute__((always_inline)) {
     // S^T = K Q^T
     f32x16_t s[KB];
-    qk_tile_b<IN, KB, NKS, ROWB>(s, kbase, slot.off, qf);
+    qk_tile<IN, KB, NKS, ROWB>(s, kbase, slot.off, qf);
     if (needs_mask(j)) {
       // register i of key block kb holds key j*BK + 8*hl + off with
       // off = kb*32 + 16*(i >> 3) + (i & 7), a constant: the key is visible
@@ -592,7 +529,7 @@ void fwd_direct(FwdArgs a) {
     // the next tile's copies go out here, between the softmax and P.V (see step)
     mid();
     // O^T += V^T P^T; consecutive MFMAs go to different accumulators
-    pv_tile_b<IN, KB, NDB, ROWB>(o, vbase, slot.off, pb);
+    pv_tile<IN, KB, NDB, ROWB>(o, vbase, slot.off, pb);
   };
 
   auto slot_ref = [&](auto S) __attribute__((always_inline)) -> RingView {
@@ -725,7 +662,7 @@ void fwd_direct8(FwdArgs a) {
   constexpr int CPT = STILE / 16 / kDirectThreads;      // staged chunks per thread
   static_assert(SLPW >= 1 && CPT >= 1, "tile mapping");
 
-  __shared__ LdsSlot<TILE_B> ring0, ring1;
+  __shared__ DirectRing<TILE_B, 2> dr;
   __shared__ Stage8<D> stage;
 
   const int tid = threadIdx.x;
@@ -766,7 +703,7 @@ void fwd_direct8(FwdArgs a) {
   };
   // widen the staged tile into a ring slot: 16 e4m3 values -> two 16-byte
   // bf16 chunks at their swizzled places
-  auto widen = [&](LdsSlot<TILE_B>& slot) __attribute__((always_inline)) {
+  auto widen = [&](const RingView& slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int ch = tid + i * kDirectThreads;
@@ -799,6 +736,26 @@ void fwd_direct8(FwdArgs a) {
   const int vrow0 = 8 * hl + (li >> 2);
   const int vswz = L::vswz(vrow0);
   const int vcol = 16 * (grp & 1) + 4 * (li & 3);
+  // the read addresses of slot 0 (as in fwd_direct)
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  uint32_t kbase[NKS], vbase[NDB];
+  {
+    const uint32_t ka = (uint32_t)(uintptr_t)(lds_u8*)&dr.k[0][0];
+    const uint32_t va = (uint32_t)(uintptr_t)(lds_u8*)&dr.v[0][0];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      kbase[ks] = ka + krow * ROWB + (((2 * ks + hl) ^ kswz) * 16);
+      asm volatile("" : "+v"(kbase[ks]));
+      kbase[ks] &= 0x3ffffu;
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int col = db * 32 + vcol;
+      vbase[db] = va + vrow0 * ROWB + (((col >> 3) ^ vswz) * 16) + ((col & 4) << 1);
+      asm volatile("" : "+v"(vbase[db]));
+      vbase[db] &= 0x3ffffu;
+    }
+  }
 
   const float c = a.c;
   float m2 = -INFINITY, lp = 0.f;
@@ -810,9 +767,9 @@ void fwd_direct8(FwdArgs a) {
   auto needs_mask = [&](int j) __attribute__((always_inline)) { return (j * BK + BK > n) || (CAUSAL && j * BK + BK - 1 > qw0); };
 
   // the compute of fwd_direct on the widened tile
-  auto compute = [&](const LdsSlot<TILE_B>& slot, int j) __attribute__((always_inline)) {
+  auto compute = [&](const RingView& slot, int j) __attribute__((always_inline)) {
     f32x16_t s[KB];
-    qk_tile<Elt::BF16, KB, NKS, ROWB>(s, slot.k, krow, kswz, hl, qf);
+    qk_tile<Elt::BF16, KB, NKS, ROWB>(s, kbase, slot.off, qf);
     if (needs_mask(j)) {
       // register i of key block kb holds key j*BK + 8*hl + off with
       // off = kb*32 + 16*(i >> 3) + (i & 7), a constant: the key is visible
@@ -859,11 +816,11 @@ void fwd_direct8(FwdArgs a) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[db] *= alpha;
     }
-    pv_tile<Elt::BF16, KB, NDB, ROWB>(o, slot.v, vrow0, vcol, vswz, pb);
+    pv_tile<Elt::BF16, KB, NDB, ROWB>(o, vbase, slot.off, pb);
   };
 
   // Step j: tile j is in `cur`; tile j + 1 is staged; tile j + 2 is copied next.
-  auto step = [&](LdsSlot<TILE_B>& cur, LdsSlot<TILE_B>& nxt, int j) __attribute__((always_inline)) {
+  auto step = [&](const RingView& cur, const RingView& nxt, int j) __attribute__((always_inline)) {
     wait_vmcnt<0>();   // this wave's share of tile j + 1 is staged
     __syncthreads();   // ... every wave's; nobody reads tile j - 1 from nxt any more
     if (j + 1 < nt) widen(nxt);
@@ -872,14 +829,10 @@ void fwd_direct8(FwdArgs a) {
     if (live(j)) compute(cur, j);
   };
 
+  const RingView r0{dr.k[0], dr.v[0], 0}, r1{dr.k[1], dr.v[1], TILE_B};
   {
-    LdsSlot<TILE_B>* slots[2] = {&ring0, &ring1};
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      u32x4_t* p = (u32x4_t*)slots[s];
-      for (int i = tid; i < (int)(sizeof(LdsSlot<TILE_B>) / 16); i += kDirectThreads)
-        p[i] = u32x4_t{0, 0, 0, 0};
-    }
+    u32x4_t* p = (u32x4_t*)&dr;
+    for (int i = tid; i < (int)(sizeof(dr) / 16); i += kDirectThreads) p[i] = u32x4_t{0, 0, 0, 0};
   }
   issue(j_lo);
   wait_vmcnt<0>();
@@ -890,12 +843,12 @@ void fwd_direct8(FwdArgs a) {
     if (a.qneg) qf[ks] ^= 0x80008000u;  // a negative scale: q -> -q
   }
   __syncthreads();
-  widen(ring0);
+  widen(r0);
   __syncthreads();
   issue(j_lo + 1);
   for (int j0 = j_lo; j0 < nt; j0 += 2) {
-    step(ring0, ring1, j0);
-    if (j0 + 1 < nt) step(ring1, ring0, j0 + 1);
+    step(r0, r1, j0);
+    if (j0 + 1 < nt) step(r1, r0, j0 + 1);
   }
   wait_vmcnt<0>();
 
