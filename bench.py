@@ -52,8 +52,10 @@ KERNEL_OF_DTYPE = {"bf16": "fwd_direct", "f16": "fwd_direct", "fp8": "fwd_direct
 # f16 / bf16 heads of d_k 128 run on the 384-row kernels (unsplit, dense
 # batches, two or more 384-row tiles per CU): causal heads of W48_PACK_MIN_N
 # <= n < W48_MIN_N on fwd_w48_packed (while every head gets two or more
-# workgroups), heads of n >= W48_MIN_N on fwd_w48; the same rule as the
-# forward dispatch in fa_fwd.hip
+# workgroups), heads of n >= W48_MIN_N on fwd_w48, and heads without the mask
+# from W48_PACK_MIN_N rows on fwd_w48 where its grid fills its rounds at
+# least 91% as well as fwd_direct's; the same rule as the forward dispatch in
+# fa_fwd.hip
 W48_PACK_MIN_N, W48_MIN_N, W48_ROWS = 6144, 16384, 384
 
 
@@ -69,6 +71,12 @@ def fwd_kernel(w, split: bool, ragged: bool = False) -> str:
                 return "fwd_w48_packed"
             if w.n >= W48_MIN_N:
                 return "fwd_w48"
+            if not w.causal and w.n >= W48_PACK_MIN_N:
+                dt = -(-w.n // 256)
+                dpair = dt % 2 == 0 and bh * (dt // 2) >= cus
+                wd, w48 = bh * (dt // 2 if dpair else dt), bh * tiles
+                if 100 * w48 * -(-wd // cus) >= 91 * wd * -(-w48 // cus):
+                    return "fwd_w48"
     return KERNEL_OF_DTYPE[w.dtype]
 # the files the forward kernels and their launch shape are compiled from; a
 # stored traffic measurement is valid only for the sources it was taken on

@@ -6,7 +6,9 @@ there are two or more 384-row tiles per compute unit (heads x tiles >= 512
 on a 256-CU device): causal heads of 6144 <= n < 16384 with the tiles packed
 into groups of near-equal length (one workgroup per group; with a multiple
 of 8 heads, each workgroup may take two or more heads in turn), heads of
-n >= 16384 with one workgroup per tile. Tiles are laid out from the last row back, so a ragged n leaves a
+n >= 16384 with one workgroup per tile, and heads without the mask from
+6144 rows with one workgroup per tile where that grid fills its rounds of
+workgroups nearly as well as the 256-row kernel's. Tiles are laid out from the last row back, so a ragged n leaves a
 partial first tile whose missing rows lie before row 0, and the softmax
 takes no chunk max unless a lane's sum of p passes 2^64 (bf16) or 2^15
 (f16). The shapes below take each path; rows are a seeded sample (the first
@@ -59,6 +61,8 @@ def _dev(t):
     ("bf16", True, 64, 8200),     # packed, 8 groups per head, two heads in turn; first tile 136 rows
     ("bf16", True, 32, 6144),     # packed, 16 full tiles in 8 groups of two
     ("f16", True, 32, 7000),      # packed, 19 tiles; first tile holds 88 rows
+    ("bf16", False, 32, 6144),    # no mask, one workgroup per tile (512 = two full rounds)
+    ("f16", False, 32, 12000),    # no mask, one workgroup per tile; first tile holds 96 rows
 ])
 def test_w48_sampled_rows(dtype, causal, heads, n):
     say(f"w48 [1, {heads}, {n}, {D}] {dtype} causal={causal}")

@@ -1725,9 +1725,23 @@ hipError_t dispatch_causal(const FwdArgs& a, hipStream_t s) {
         const unsigned grid = (unsigned)(a.bh / wa.plan.heads_seq * wa.plan.bins);
         return launch_kernel(fwd_w48_packed<E>, dim3(grid), dim3(kW48Threads), s, wa);
       }
-      // otherwise one workgroup per tile for long heads (n >= FA_W48_MIN_N),
-      // where that measured faster than the 256-row kernel
-      if (dense && a.n >= FA_W48_MIN_N) {
+      // otherwise one workgroup per tile: for long heads (n >= FA_W48_MIN_N),
+      // and, without the mask, from FA_W48_PACK_MIN_N rows where its grid
+      // fills its rounds of workgroups at least 91% as well as the 256-row
+      // kernel's does (its rounds run ~12% faster; measured +3% to +24% at
+      // 6144 <= n <= 12288, -6% at 48 heads of 8192 (fill ratio 0.83) and
+      // -3% at 32 heads of 7000 (0.905))
+      bool w48_fill = false;
+      if (dense && !a.causal && a.n >= FA_W48_PACK_MIN_N && a.n < FA_W48_MIN_N) {
+        const long c = cus, w48 = (long)a.bh * wt;
+        const int dt = (a.n + kDirectBq - 1) / kDirectBq;
+        const bool dpair = dt % 2 == 0 && FA_PAIR_TILES_NOMASK && FA_STAGES == 2 && (long)a.bh * (dt / 2) >= c;
+        const long wd = (long)a.bh * (dpair ? dt / 2 : dt);
+        const long r48 = (w48 + c - 1) / c, rd = (wd + c - 1) / c;  // rounds
+        // fill(w48) >= 0.91 fill(direct), fill = workgroups / (rounds * CUs)
+        w48_fill = 100 * w48 * rd >= 91 * wd * r48;
+      }
+      if (dense && (a.n >= FA_W48_MIN_N || w48_fill)) {
         const dim3 grid((unsigned)a.bh * (unsigned)wt, 1u);
         return a.causal ? launch_kernel(fwd_w48<E, true>, grid, dim3(kW48Threads), s, a)
                         : launch_kernel(fwd_w48<E, false>, grid, dim3(kW48Threads), s, a);
