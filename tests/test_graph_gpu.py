@@ -45,6 +45,28 @@ def test_forward_replays(causal):
         assert torch.equal(out, o_ref) and torch.equal(lse, lse_ref), rep
 
 
+@pytest.mark.parametrize("heads,n,causal", [(32, 8192, True), (12, 16500, False)])
+def test_384_row_kernels_replay(heads, n, causal):
+    """The 384-row kernels: the packed causal launch (its host-built plan of
+    tile groups travels in the captured kernel arguments) and one workgroup
+    per tile."""
+    say(f"graph replay, fa_forward [1, {heads}, {n}, 128] causal={causal}")
+    d = workload.make_inputs(1, heads, n, 128, "bf16", seed=33).to("cuda")
+    o_ref, lse_ref = fa.forward(d.q, d.k, d.v, causal=causal)
+    out, lse = torch.empty_like(o_ref), torch.empty_like(lse_ref)
+    q2, k2, v2 = (x[:, :, :6000].contiguous() for x in (d.q, d.k, d.v))
+    g = _capture(lambda: fa.forward(d.q, d.k, d.v, causal=causal, out=out, lse=lse))
+    for rep in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        # eager work between replays: a call of another shape (another plan)
+        fa.forward(q2, k2, v2, causal=True)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_ref) and torch.equal(lse, lse_ref), rep
+
+
 def test_splitkv_replays():
     say("graph replay, fa_forward_splitkv (blocks + merge)")
     d = workload.make_inputs(1, 2, 2048, 128, "bf16", seed=32).to("cuda")
