@@ -99,16 +99,20 @@ def test_w48_growing_scores(dtype, causal, n):
     check_rows(inp, causal, rows)
 
 
-def test_w48_strided_is_bitwise_dense():
+@pytest.mark.parametrize("heads,n,causal", [
+    (12, 16500, True),   # one workgroup per tile
+    (12, 16200, True),   # packed
+    (32, 6144, False),   # no mask, one workgroup per tile
+])
+def test_w48_strided_is_bitwise_dense(heads, n, causal):
     """[batch, n, heads, d_k] inputs and output give bitwise the dense result."""
     import transformer_attention_08_amd as fa
-    n, heads = 16500, 12
-    say(f"w48 strided [1, {n}, {heads}, {D}] bf16 causal")
+    say(f"w48 strided [1, {n}, {heads}, {D}] bf16 causal={causal}")
     inp = workload.make_inputs(1, heads, n, D, "bf16", seed=31)
     q, k, v = _dev(inp.q), _dev(inp.k), _dev(inp.v)
-    o1, l1 = fa.forward(q, k, v, causal=True)
+    o1, l1 = fa.forward(q, k, v, causal=causal)
     qs, ks, vs = (t.transpose(1, 2).contiguous() for t in (q, k, v))
-    o2, l2 = fa.forward_strided(qs, ks, vs, layout="bshd", causal=True)
+    o2, l2 = fa.forward_strided(qs, ks, vs, layout="bshd", causal=causal)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2.transpose(1, 2)) and torch.equal(l1, l2)
 
